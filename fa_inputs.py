@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+Shared by both sides of every parity check (the HIP path and the fp64
+oracle) and by the benchmark.  It holds none of the method's arithmetic:
+only random draws, rounding of the draws to the storage type, row sampling
+and the workload table.
+
+Recipe (stated once, used everywhere):
+  * numpy ``Generator(PCG64)``; the three tensors Q, K, V get the streams
+    ``SeedSequence(seed).spawn(3)`` in that order;
+  * each element is ``standard_normal(dtype=float32) * sigma``;
+  * for bf16 / fp16 storage the fp32 draw is rounded to nearest-even
+    (bf16 kept as its 16-bit pattern, a uint16 array).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DTYPES = ("f32", "bf16", "f16")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bit patterns.
+    NaN stays NaN (quiet), infinities stay infinities."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _draw(rng: np.random.Generator, shape, sigma: float, dtype: str, chunk: int = 1 << 24):
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        out = np.empty(n, dtype=np.float32)
+    elif dtype == "f16":
+        out = np.empty(n, dtype=np.float16)
+    elif dtype == "bf16":
+        out = np.empty(n, dtype=np.uint16)
+    else:
+        raise ValueError(dtype)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        if dtype == "f32":
+            out[s:e] = x
+        elif dtype == "f16":
+            out[s:e] = x.astype(np.float16)  # numpy rounds to nearest-even
+        else:
+            out[s:e] = f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+def make_qkv(B: int, H: int, N: int, D: int, dtype: str, seed: int,
+             sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0):
+    """Q, K, V of shape [B, H, N, D] in storage form (float32, float16 or bf16 bits)."""
+    ss = np.random.SeedSequence(seed).spawn(3)
+    shape = (B, H, N, D)
+    q = _draw(np.random.Generator(np.random.PCG64(ss[0])), shape, sigma_q, dtype)
+    k = _draw(np.random.Generator(np.random.PCG64(ss[1])), shape, sigma_k, dtype)
+    v = _draw(np.random.Generator(np.random.PCG64(ss[2])), shape, sigma_v, dtype)
+    return q, k, v
+
+
+def sample_rows(N: int, n_rows: int, seed: int) -> np.ndarray:
+    """Sorted query positions: 0 and N-1 always, the rest drawn without replacement."""
+    if n_rows >= N:
+        return np.arange(N, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = {0, N - 1}
+    rest = rng.choice(np.arange(1, N - 1), size=max(0, n_rows - len(fixed)), replace=False)
+    return np.array(sorted(fixed.union(int(r) for r in rest)), dtype=np.int64)
+
+
+def sample_slices(B: int, H: int, n: int, seed: int):
+    """n distinct (b, h) pairs drawn without replacement, sorted."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    flat = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(f) // H, int(f) % H) for f in sorted(flat)]
+
+
+# The five synthetic workloads.  "check" says which query rows the oracle
+# evaluates: "full" (every row of every slice), or ("rows", n) per slice, or
+# ("slices_rows", n_slices, n_rows).
+WORKLOADS = {
+    "tiny_f32": dict(B=1, H=1, N=128, D=64, dtype="f32", modes=(False,), seed=1001,
+                     sigma=(1.0, 1.0, 1.0), check=("full",)),
+    "small_bf16": dict(B=2, H=8, N=1024, D=64, dtype="bf16", modes=(False, True), seed=1002,
+                       sigma=(1.0, 1.0, 1.0), check=("full",)),
+    "small_f32": dict(B=2, H=8, N=1024, D=64, dtype="f32", modes=(False, True), seed=1003,
+                      sigma=(1.0, 1.0, 1.0), check=("full",)),
+    "headline_bf16": dict(B=4, H=16, N=4096, D=128, dtype="bf16", modes=(False, True), seed=1004,
+                          sigma=(1.0, 1.0, 1.0), check=("rows", 256)),
+    "wide_bf16": dict(B=32, H=32, N=4096, D=64, dtype="bf16", modes=(False,), seed=1005,
+                      sigma=(1.0, 1.0, 1.0), check=("slices_rows", 8, 128)),
+    "long_causal_bf16": dict(B=1, H=8, N=131072, D=128, dtype="bf16", modes=(True,), seed=1006,
+                             sigma=(0.5, 0.5, 1.0), check=("rows", 64)),
+}
+
+
+def workload_flops(B: int, H: int, N: int, D: int, causal: bool) -> float:
+    """The metric's FLOP count: 4*B*H*N^2*D, halved for causal."""
+    f = 4.0 * B * H * N * N * D
+    return f / 2 if causal else f
