@@ -1,0 +1,253 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+One step = one fa_fwd call over the whole workload (the full hot path:
+Q/K/V tiles -> scores -> online softmax -> P V -> O and lse), inputs already
+resident in HBM.  Default workload: B4 H16 N4096 D128, bf16, non-causal.
+Throughput counts 4*B*H*N^2*D FLOPs per step (half for causal).
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, B4 H16 N4096 D128"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", "fa_fwd.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_mfma_bf16_d128_B4H16N4096_counters.txt")
+
+WORKLOADS = {
+    # name: (B, H, N, D, dtype, causal, sigma)
+    "headline": (4, 16, 4096, 128, "bf16", False, (1.0, 1.0, 1.0)),
+    "headline_causal": (4, 16, 4096, 128, "bf16", True, (1.0, 1.0, 1.0)),
+    "small": (2, 8, 1024, 64, "bf16", False, (1.0, 1.0, 1.0)),
+    "small_causal": (2, 8, 1024, 64, "bf16", True, (1.0, 1.0, 1.0)),
+    "small_f32": (2, 8, 1024, 64, "f32", False, (1.0, 1.0, 1.0)),
+    "tiny_f32": (1, 1, 128, 64, "f32", False, (1.0, 1.0, 1.0)),
+    "wide": (32, 32, 4096, 64, "bf16", False, (1.0, 1.0, 1.0)),
+    "long_causal": (1, 8, 131072, 128, "bf16", True, (0.5, 0.5, 1.0)),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    if not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def device_inputs(B, H, N, D, dtype, sigma, seed=1004):
+    import numpy as np
+    import torch
+
+    import fa_inputs as fi
+    q, k, v = fi.make_qkv(B, H, N, D, dtype, seed, *sigma)
+
+    def up(x):
+        if dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(x).to("cuda")
+    return (q, k, v), tuple(up(x) for x in (q, k, v))
+
+
+def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded row sample of the same workload;
+    also checks those rows of the GPU output.  Returns the JSON object."""
+    import numpy as np
+
+    import fa_inputs as fi
+    import oracle
+    q, k, v = host_qkv
+    o_dev, lse_dev = dev_out
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    scale = oracle.gpu_scale(1.0 / math.sqrt(D))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    o_host = o_dev.view(-1).cpu()
+    l_host = lse_dev.view(-1).cpu().numpy()
+    import torch
+    o_bits = o_host.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else o_host.numpy()
+    o_np = o_bits.reshape(B, H, N, D)
+    l_np = l_host.reshape(B, H, N)
+
+    def run(rows_per_head, nheads):
+        flops = 0.0
+        worst_o = worst_l = 0.0
+        t0 = time.perf_counter()
+        for (b, h) in heads[:nheads]:
+            rows = fi.sample_rows(N, rows_per_head, seed=77 + 100 * b + h)
+            qw = oracle.widen(q[b, h][rows], dtype)
+            kw = oracle.widen(k[b, h], dtype)
+            vw = oracle.widen(v[b, h], dtype)
+            o_ref, l_ref = oracle.attention_rows(qw, kw, vw, rows, scale, causal, n_threads=threads)
+            nk = (rows + 1) if causal else np.full(rows.shape, N)
+            flops += float(np.sum(4.0 * nk * D))
+            worst_o = max(worst_o, float(np.abs(oracle.widen(o_np[b, h][rows], dtype) - o_ref).max()))
+            worst_l = max(worst_l, float(np.abs(l_np[b, h][rows].astype(np.float64) - l_ref).max()))
+        return time.perf_counter() - t0, flops, worst_o, worst_l
+
+    # calibrate on a tiny sample, then size the sample to about budget_s seconds
+    t, f, _, _ = run(8, min(4, len(heads)))
+    rate = f / max(t, 1e-6)
+    per_head = 4.0 * N * D * (N / 2 if causal else N)  # flops for all rows of one head
+    total_rows = max(8, int(budget_s * rate / (per_head / N)))
+    nheads = len(heads)
+    rows_per_head = max(2, min(N, total_rows // nheads))
+    t, f, eo, el = run(rows_per_head, nheads)
+    log("cpu oracle: %d heads x %d rows, %.2f s, %.3f GFLOP/s, %d threads; sampled GPU rows max|dO|=%.3g max|dlse|=%.3g"
+        % (nheads, rows_per_head, t, f / t / 1e9, threads, eo, el))
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d heads x %d seeded query rows (all %d keys%s), fp64 three-pass oracle, %.1f s"
+                      % (nheads, rows_per_head, N, ", causal prefix" if causal else "", t),
+            "check_max_abs_dO": eo, "check_max_abs_dlse": el}
+
+
+def bench_one(name, steps, warmup, with_cpu, copy_calibration=False):
+    import torch
+
+    import attention_fa_fwd_02_amd as fa
+    import fa_inputs as fi
+    B, H, N, D, dtype, causal, sigma = WORKLOADS[name]
+    host, (q, k, v) = device_inputs(B, H, N, D, dtype, sigma)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    code = {"f32": fa.FA_DTYPE_F32, "bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[dtype]
+    scale = 1.0 / math.sqrt(D)
+
+    def step():
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, N, D, scale, int(causal), code, stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    if copy_calibration:
+        # a plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kern_ms = sum(per) / len(per)
+    flops = fi.workload_flops(B, H, N, D, causal)
+    ms_per_step = total_ms / steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    log("%s: B%d H%d N%d D%d %s causal=%d  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
+        % (name, B, H, N, D, dtype, causal, ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
+           100 * achieved / peak, dtype))
+    res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
+               kernel_ms=kern_ms, value=value, achieved=achieved, peak=peak, flops=flops)
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(host, (o, lse), B, H, N, D, dtype, causal)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy first (for scaling HBM byte counters)")
+    ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(each (batch, head) slice is independent; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    main_res = bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
+                         args.copy_calibration)
+    if args.all:
+        for name in WORKLOADS:
+            if name != args.workload:
+                bench_one(name, max(3, args.steps // 5), 2, False)
+
+    r = main_res
+    traffic = read_traffic() if r["name"] == "headline" else None
+    out = {
+        "metric": METRIC,
+        "value": round(r["value"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "B%d H%d N%d D%d %s %s" % (r["B"], r["H"], r["N"], r["D"], r["dtype"],
+                                                          "causal" if r["causal"] else "non-causal"),
+                   "B": r["B"], "H": r["H"], "N": r["N"], "D": r["D"], "causal": r["causal"],
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100.0 * r["achieved"] / r["peak"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 3), "peak": r["peak"],
+                     "unit": "TFLOP/s", "frac": round(r["achieved"] / r["peak"], 4),
+                     "traffic": traffic,
+                     "kernel": "fa_fwd_mfma_kernel<%s, D=%d, causal=%d>" % (r["dtype"], r["D"], r["causal"]),
+                     "kernel_avg_ms": round(r["kernel_ms"], 5)},
+        "cpu_baseline": r.get("cpu_baseline"),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

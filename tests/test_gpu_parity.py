@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs with fa_inputs, runs fa_fwd on the device
+with O and lse poisoned with NaN and followed by guard bands, then compares
+element by element with the oracle on the same inputs: every row for sizes
+the oracle finishes in seconds, seeded row samples at the full workload
+sizes.  Tolerances (max-abs): fp32 path 1e-5 on O and lse; bf16 / fp16 paths
+1e-2 on O and 1e-3 on lse.
+
+Two derived adjustments:
+  * an O element whose exact value has |O| >= 4 cannot in general be stored
+    in bf16 within 1e-2 (half an ulp there is 2^-6 = 0.0156), so such
+    elements get 1e-2 plus half an ulp of the output format;
+  * the fp32 score error grows with |scale| * sum_d |q_d k_d|; the 1e-5 bound
+    holds at scale = 1/sqrt(D) and is scaled by max(1, |scale| * sqrt(D)) for
+    other scales.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3)}
+GUARD = 4096  # elements after each output that must stay untouched
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _to_device(x, dtype):
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to("cuda")
+
+
+def _tdtype(dtype):
+    torch = _torch()
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+
+
+def _host_widen(t, dtype):
+    """Device output -> float64 numpy (exact)."""
+    torch = _torch()
+    if dtype == "bf16":
+        return oracle.widen(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_fa(q, k, v, dtype, scale, causal, stream=None):
+    """Launch fa_fwd through the C ABI with poisoned, guard-banded outputs."""
+    import attention_fa_fwd_02_amd as fa
+    torch = _torch()
+    B, H, N, D = q.shape
+    n_o, n_l = B * H * N * D, B * H * N
+    td = _tdtype(dtype)
+    o_buf = torch.full((n_o + GUARD,), float("nan"), dtype=td, device="cuda")
+    l_buf = torch.full((n_l + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+    o_buf[n_o:] = 7.0
+    l_buf[n_l:] = -3.0
+    dq, dk, dv = (_to_device(x, dtype) for x in (q, k, v))
+    code = {"f32": fa.FA_DTYPE_F32, "bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[dtype]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    print("fa_fwd B%d H%d N%d D%d %s causal=%d scale=%g" % (B, H, N, D, dtype, causal, scale),
+          flush=True)
+    st = fa.fa_fwd(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), o_buf.data_ptr(), l_buf.data_ptr(),
+                   B, H, N, D, float(scale), int(causal), code, s.cuda_stream)
+    assert st == fa.FA_OK, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[n_o:] == 7.0), "O guard band overwritten"
+    assert torch.all(l_buf[n_l:] == -3.0), "lse guard band overwritten"
+    o = o_buf[:n_o].view(B, H, N, D)
+    lse = l_buf[:n_l].view(B, H, N)
+    assert bool(torch.isfinite(o).all()), "O has unwritten or non-finite elements"
+    assert bool(torch.isfinite(lse).all()), "lse has unwritten or non-finite elements"
+    return o, lse
+
+
+def half_ulp(x, dtype):
+    """Half an ulp of the output format at |x| (0 for fp32: not an output-rounding bound)."""
+    if dtype == "f32":
+        return np.zeros_like(x)
+    mant = {"bf16": 8, "f16": 11}[dtype]  # significand bits incl. the implicit one
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return np.ldexp(1.0, (e - mant).astype(np.int64))
+
+
+def compare(q, k, v, dtype, scale, causal, o_dev, lse_dev, slices, rows_of, tol_o):
+    """Oracle on the chosen (b, h) slices and rows.  Returns (max|dO|, max|dlse|,
+    max|O|, worst excess of |dO| over its per-element tolerance, #elements with |O| >= 4)."""
+    sc = oracle.gpu_scale(scale)
+    worst_o = worst_l = max_o = 0.0
+    excess = -np.inf
+    n_big = 0
+    for (b, h) in slices:
+        rows = rows_of(b, h)
+        qw = oracle.widen(q[b, h][rows], dtype)
+        kw = oracle.widen(k[b, h], dtype)
+        vw = oracle.widen(v[b, h], dtype)
+        o_ref, l_ref = oracle.attention_rows(qw, kw, vw, rows, sc, causal)
+        o_got = _host_widen(o_dev[b, h][rows_as_index(rows)], dtype)
+        l_got = lse_dev[b, h][rows_as_index(rows)].cpu().numpy().astype(np.float64)
+        d_o = np.abs(o_got - o_ref)
+        big = np.abs(o_ref) >= 4.0
+        tol = tol_o + np.where(big, half_ulp(o_ref, dtype), 0.0)
+        excess = max(excess, float((d_o - tol).max()))
+        n_big += int(big.sum())
+        worst_o = max(worst_o, float(d_o.max()))
+        worst_l = max(worst_l, float(np.abs(l_got - l_ref).max()))
+        max_o = max(max_o, float(np.abs(o_ref).max()))
+    return worst_o, worst_l, max_o, excess, n_big
+
+
+def rows_as_index(rows):
+    torch = _torch()
+    return torch.from_numpy(np.asarray(rows, dtype=np.int64)).to("cuda")
+
+
+def check_case(B, H, N, D, dtype, causal, seed, sigma=(1.0, 1.0, 1.0), scale=None,
+               slices=None, n_rows=None, row_seed=0):
+    q, k, v = fi.make_qkv(B, H, N, D, dtype, seed, *sigma)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o, lse = run_fa(q, k, v, dtype, scale, causal)
+    if slices is None:
+        slices = [(b, h) for b in range(B) for h in range(H)]
+    if n_rows is None:
+        rows_of = lambda b, h: np.arange(N, dtype=np.int64)
+    else:
+        rows_of = lambda b, h: fi.sample_rows(N, n_rows, seed=row_seed + 1000 * b + h)
+    to, tl = TOL[dtype]
+    if dtype == "f32":
+        f = max(1.0, abs(scale) * math.sqrt(D))
+        to, tl = to * f, tl * f
+    eo, el, mo, ex, nbig = compare(q, k, v, dtype, scale, causal, o, lse, slices, rows_of, to)
+    print("  max|dO|=%.3g max|dlse|=%.3g max|O|=%.3g  tol O %.3g lse %.3g  (%d elements with |O|>=4)"
+          % (eo, el, mo, to, tl, nbig), flush=True)
+    assert ex <= 0.0, (eo, to, ex)
+    assert el <= tl, (el, tl)
+    return o, lse
+
+
+# ---------------------------------------------------------------- workloads
+
+def _w(name):
+    return fi.WORKLOADS[name]
+
+
+def test_tiny_f32():
+    w = _w("tiny_f32")
+    check_case(w["B"], w["H"], w["N"], w["D"], "f32", False, w["seed"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("name", ["small_bf16", "small_f32"])
+def test_small(name, causal):
+    w = _w(name)
+    check_case(w["B"], w["H"], w["N"], w["D"], w["dtype"], causal, w["seed"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_f16(causal):
+    w = _w("small_bf16")
+    check_case(w["B"], w["H"], w["N"], w["D"], "f16", causal, w["seed"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_headline_sampled(causal):
+    w = _w("headline_bf16")
+    check_case(w["B"], w["H"], w["N"], w["D"], "bf16", causal, w["seed"], n_rows=256, row_seed=11)
+
+
+def test_wide_sampled():
+    w = _w("wide_bf16")
+    slices = fi.sample_slices(w["B"], w["H"], 8, seed=12)
+    check_case(w["B"], w["H"], w["N"], w["D"], "bf16", False, w["seed"], slices=slices,
+               n_rows=128, row_seed=13)
+
+
+def test_long_causal_sampled():
+    w = _w("long_causal_bf16")
+    check_case(w["B"], w["H"], w["N"], w["D"], "bf16", True, w["seed"], sigma=w["sigma"],
+               n_rows=64, row_seed=14)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("N", [1, 2, 31, 100, 129, 255, 257, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged(N, D, dtype, causal):
+    check_case(2, 3, N, D, dtype, causal, seed=100 + N + D)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+def test_scale_values(dtype, scale):
+    for causal in (False, True):
+        check_case(1, 2, 300, 64, dtype, causal, seed=7, scale=scale)
+
+
+def test_ragged_long_tail():
+    check_case(1, 2, 4097, 128, "bf16", False, seed=8, n_rows=200)
+    check_case(1, 2, 4097, 128, "bf16", True, seed=8, n_rows=200)
+
+
+def test_deterministic():
+    torch = _torch()
+    q, k, v = fi.make_qkv(2, 4, 1500, 128, "bf16", seed=9)
+    o1, l1 = run_fa(q, k, v, "bf16", 0.088, True)
+    o2, l2 = run_fa(q, k, v, "bf16", 0.088, True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_uniform_values_full_size():
+    """V = 1 gives O = 1 in every element (property at any size): full headline shape."""
+    torch = _torch()
+    w = _w("headline_bf16")
+    q, k, _ = fi.make_qkv(w["B"], w["H"], w["N"], w["D"], "bf16", seed=w["seed"])
+    ones = np.full(q.shape, 0x3F80, dtype=np.uint16)
+    for causal in (False, True):
+        o, lse = run_fa(q, k, ones, "bf16", 1 / math.sqrt(128), causal)
+        err = float((o.float() - 1.0).abs().max())
+        print("  uniform V: max|O-1| = %.3g" % err, flush=True)
+        assert err <= 1e-2
+
+
+def test_side_stream_and_binding():
+    """The convenience binding on a non-default stream matches the default-stream result."""
+    import attention_fa_fwd_02_amd as fa
+    torch = _torch()
+    q, k, v = fi.make_qkv(1, 2, 700, 64, "bf16", seed=10)
+    dq, dk, dv = (_to_device(x, "bf16") for x in (q, k, v))
+    o_ref, l_ref = fa.fwd(dq, dk, dv, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fwd(dq, dk, dv, causal=True)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o_ref.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l_ref, l2)
