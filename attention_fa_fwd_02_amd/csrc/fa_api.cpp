@@ -117,7 +117,10 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     args.N = (int32_t)N;
     args.n_qblk = (int32_t)((N + fa::kQueryBlock - 1) / fa::kQueryBlock);
     const float log2e = 1.44269504088896340736f;
-    args.c = std::fabs(scale) * log2e;
+    // c > 0 always: for |scale| * log2(e) below 1e-30 every weight exp2(c*s - m) is
+    // exactly 1.0f, the same as for scale = 0, and masked scores (-inf) give
+    // exp2(-inf) = 0 instead of the NaN that -inf * 0 would produce
+    args.c = std::fmax(std::fabs(scale) * log2e, 1e-30f);
     args.qneg = std::signbit(scale) ? (dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u) : 0u;
     const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, B * H, args,
                                           reinterpret_cast<hipStream_t>(stream));
