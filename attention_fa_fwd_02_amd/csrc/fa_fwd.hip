@@ -89,6 +89,27 @@ __device__ __forceinline__ int row_perm(int r) {
     return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
+// Workgroup barrier without the memory fence __syncthreads() adds: the fence
+// waits for every outstanding global load (vmcnt(0)), including direct-to-LDS
+// loads issued ahead for later tiles.  Callers wait for the loads that must
+// have landed (s_waitcnt vmcnt(n)) before calling; every LDS read of the
+// current tile has been consumed by an MFMA before the barrier is reached.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 16, "vmcnt fits the low field");
+    __builtin_amdgcn_s_waitcnt(0xF70 | n);
+}
+
 // Max / sum over the lane pair (l, l^32) that shares one query row.
 __device__ __forceinline__ float pair_max(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -156,11 +177,22 @@ struct MfmaCfg {
     static constexpr int BC = (D == 64) ? 128 : 64; // keys per tile (K and V tiles are 16 KB each)
     static constexpr int KP = 2 * D + 16;           // K row pitch in LDS (bytes)
     static constexpr int VP = 2 * D + 32;           // V row pitch in LDS (bytes)
+    // tiles arrive by direct-to-LDS loads: one instruction fills 1 KB (64 lanes x
+    // 16 bytes) of consecutive LDS, so a padded tile is a whole number of 1 KB blocks
+    static constexpr int NK = BC * KP / 1024;       // K blocks per tile
+    static constexpr int NV = BC * VP / 1024;       // V blocks per tile
+    static_assert(NK * 1024 == BC * KP && NV * 1024 == BC * VP, "tiles are whole 1 KB blocks");
+    // every wave issues the same number of loads per tile, so that the number in
+    // flight is a compile-time constant; the spare blocks land past the V region
+    static constexpr int LPW = (NK + NV + kWaves - 1) / kWaves; // loads per wave and tile
     static constexpr int KST = BC * KP;
-    static constexpr int STAGE = KST + BC * VP;
+    static constexpr int STAGE = 1024 * kWaves * LPW;
+    static_assert(KST + BC * VP <= STAGE, "K and V regions fit in a stage");
     static constexpr int OP = 2 * D + 16;           // O staging row pitch (bytes)
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int STAGES = 3;
+    static constexpr int LDS = STAGES * STAGE;
     static_assert(kWaves * 32 * OP <= LDS, "O staging fits in the tile buffers");
+    static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
 };
 
 template <typename E, int D, bool CAUSAL>
@@ -174,12 +206,19 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
     constexpr float kTau = 8.0f; // deferred-rescale threshold (log2 units)
     static_assert(BC * KCH == 2 * kThreads, "K and V tiles = two 16-byte chunks per thread each");
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    lds_char *const smem = (lds_char *)smem_raw;
+    // Three tile stages as separate LDS objects: the compiler can then tell
+    // that the direct-to-LDS loads into one stage do not alias the reads of
+    // another, and does not wait for them before every LDS read.
+    __shared__ __attribute__((aligned(16))) char stage0_raw[Cfg::STAGE];
+    __shared__ __attribute__((aligned(16))) char stage1_raw[Cfg::STAGE];
+    __shared__ __attribute__((aligned(16))) char stage2_raw[Cfg::STAGE];
+    lds_char *const stage0 = (lds_char *)stage0_raw;
+    lds_char *const stage1 = (lds_char *)stage1_raw;
+    lds_char *const stage2 = (lds_char *)stage2_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31;
     const int g = lane >> 5;
     const int N = a.N;
@@ -198,36 +237,41 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int kv_end = CAUSAL ? min(N, q0 + kQueryBlock) : N;
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    // --- tile loader: 16-byte chunk c = tid + 512*i is row c / KCH, chunk c % KCH;
-    // a wave covers whole rows (coalesced global reads, conflict-free LDS writes)
-    int lrow[2], lcol[2];
+    // --- tile loader: direct global -> LDS loads ------------------------------
+    // Load j of wave w fills 1 KB block b = w + 8j of the stage: lane l writes
+    // stage byte 1024 b + 16 l.  Blocks below NK hold the K tile (row pitch KP),
+    // the next NV the V tile (pitch VP), the rest are spare.  A lane whose slot
+    // falls in a row's padding re-reads the row's first chunk, a row at or past
+    // kv_end re-reads row kv_end-1 (its scores are masked, its weights 0), and a
+    // spare block re-reads the tile's first K row; none of these bytes is read
+    // back.  Every tile issues its loads unconditionally, also the two tiles
+    // past the last (they re-read row kv_end-1 into stages nobody reads again),
+    // so that each wave has exactly LPW loads in flight at every barrier.
+    constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
+    const uint16_t *src[LPW];
+    int srow[LPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + kThreads * i;
-        lrow[i] = c / KCH;
-        lcol[i] = c % KCH;
+    for (int j = 0; j < LPW; ++j) {
+        const int blk = wave + kWaves * j;
+        const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
+        const int pitch = is_k ? KP : VP;
+        const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
+        const int chunk = (pos % pitch) / 16;
+        const int off = chunk < KCH ? 8 * chunk : 0;
+        srow[j] = (is_k || is_v) ? pos / pitch : 0;
+        src[j] = (is_v ? V : K) + ((is_k || is_v) ? off : 0);
     }
-    u32x4 kr[2], vr[2];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    auto load_tile = [&](int t) {
+    auto issue_tile = [&](int t, lds_char *st) {
         const int k0 = t * BC;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int key = k0 + lrow[i];
-            const int64_t off = (int64_t)key * D + lcol[i] * 8;
-            kr[i] = key < N ? *(const u32x4 *)(K + off) : zero4;
-            vr[i] = key < N ? *(const u32x4 *)(V + off) : zero4;
+        for (int j = 0; j < LPW; ++j) {
+            const int key = min(k0 + srow[j], kv_end - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(src[j] + (int64_t)key * D),
+                                             (__attribute__((address_space(3))) void *)(st + 1024 * (wave + kWaves * j)),
+                                             16, 0, 0);
         }
     };
-    auto store_tile = [&](int stage) {
-        lds_char *ks = smem + stage * Cfg::STAGE;
-        lds_char *vs = ks + Cfg::KST;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *(__attribute__((address_space(3))) u32x4 *)(ks + lrow[i] * KP + lcol[i] * 16) = kr[i];
-            *(__attribute__((address_space(3))) u32x4 *)(vs + lrow[i] * VP + lcol[i] * 16) = vr[i];
-        }
-    };
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     // --- per-lane LDS read bases --------------------------------------------
     // score MFMA A operand: row r of a 32-key block is key 8(r/8) + 2(r%4) + (r/4)%2,
@@ -254,30 +298,29 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     float l_run = 0.f;       // this lane's share of the exp2-sum against m_run
     const float c = a.c;     // > 0 (the host clamps it)
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int stage = t & 1;
-        if (t + 1 < n_tiles)
-            load_tile(t + 1);
+    // one tile: issue the loads of tile t+2 into the stage tile t-1 used (free
+    // since the last barrier), compute tile t from stage `cur`, then make tile
+    // t+1 visible
+    auto tile = [&](int t, const lds_char *cur, lds_char *next2) {
+        issue_tile(t + 2, next2);
         const int k0 = t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
         if (active) {
-            const lds_char *ks = smem + stage * Cfg::STAGE + k_lane;
-            const lds_char *vs = smem + stage * Cfg::STAGE + Cfg::KST + v_lane;
+            const lds_char *ks = cur + k_lane;
+            const lds_char *vs = cur + Cfg::KST + v_lane;
             // S^T = K Q^T : s[kb][i] = score(query qi, key k0 + 32kb + 2i + g)
+            // (the KB accumulation chains advance together)
             f32x16 s[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+            for (int kb = 0; kb < KB; ++kb)
                 s[kb] = f32x16{};
 #pragma unroll
-                for (int cc = 0; cc < DC; ++cc) {
+            for (int cc = 0; cc < DC; ++cc)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
                     const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(ks + 32 * kb * KP + 32 * cc);
                     s[kb] = E::mfma(kv, qf[cc], s[kb]);
                 }
-            }
             // masking: keys beyond N, and keys after the query when causal
             if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
 #pragma unroll
@@ -338,15 +381,41 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                         o[b] = E::mfma(vv, pb, o[b]);
                     }
         }
-        if (t + 1 < n_tiles)
-            store_tile(stage ^ 1);
-        __syncthreads();
+        // this wave's loads of tile t+1 have landed once only those of tile t+2
+        // are in flight; the barrier then publishes tile t+1 to every wave
+        wait_vmcnt<LPW>();
+        tile_barrier();
+    };
+
+    // tiles 0 and 1 in flight; tile 0 complete before the first barrier
+    issue_tile(0, stage0);
+    issue_tile(1, stage1);
+    wait_vmcnt<LPW>();
+    tile_barrier();
+    // tile t lives in stage t % 3.  Whole groups of three tiles run in the
+    // loop, with no exit between them, and the one or two left over after it:
+    // every access then names its stage object statically, and on every path
+    // into a tile only loads of the other two stages can still be in flight.
+    int t = 0;
+    for (; t + 3 <= n_tiles; t += 3) {
+        tile(t, stage0, stage2);
+        tile(t + 1, stage1, stage0);
+        tile(t + 2, stage2, stage1);
     }
+    if (t < n_tiles) {
+        tile(t, stage0, stage2);
+        if (t + 1 < n_tiles)
+            tile(t + 1, stage1, stage0);
+    }
+    // the loads past the last tile must land before stages 0 and 1 are reused
+    wait_vmcnt<0>();
+    tile_barrier();
 
     // --- epilogue: O / l staged through LDS (wave-private rows), lse ---------
     const float l_tot = pair_sum(l_run);
     const float inv = 1.0f / l_tot;
-    lds_char *ow = smem + wave * 32 * OP;
+    static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
+    lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
     if (q0w < N) {
 #pragma unroll
         for (int b = 0; b < OB; ++b)
@@ -581,9 +650,10 @@ hipError_t launch_f32(int64_t nwg, const FwdArgs &args, hipStream_t stream) {
 
 template <typename E, int D>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
+    // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     if (causal)
-        return launch(fa_fwd_mfma_kernel<E, D, true>, nwg, MfmaCfg<D>::LDS, args, stream);
-    return launch(fa_fwd_mfma_kernel<E, D, false>, nwg, MfmaCfg<D>::LDS, args, stream);
+        return launch(fa_fwd_mfma_kernel<E, D, true>, nwg, 0, args, stream);
+    return launch(fa_fwd_mfma_kernel<E, D, false>, nwg, 0, args, stream);
 }
 
 } // namespace
