@@ -81,6 +81,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.693147180559945309f;
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data format,
+// no swizzle, so loads address plain bytes and are range-checked against the
+// descriptor's record count (out-of-range loads return zeros).
+constexpr int kBufferWord3 = 0x00020000;
 
 // Row order inside a 32-row fp32 MFMA operand block: accumulator row
 // 8a + 4g + b (a = item / 4, b = item % 4, g = lane / 32) maps to 16g + 4a + b,
@@ -108,6 +112,16 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(n >= 0 && n < 16, "vmcnt fits the low field");
     __builtin_amdgcn_s_waitcnt(0xF70 | n);
+}
+
+// Direct global -> LDS load of 16 bytes per lane through a buffer descriptor
+// over [base, base + bytes): lane l's bytes from offset voff land at LDS
+// address lds + 16 l (lds is wave-uniform).  Offsets at or past `bytes` read
+// zeros and touch no memory.
+__device__ __forceinline__ void load_lds_16(const void *base, uint32_t bytes, uint32_t voff, lds_char *lds) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
 }
 
 // Max / sum over the lane pair (l, l^32) that shares one query row.
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr int OB = D / 32;  // 32-feature blocks of O
     constexpr int KCH = D / 8;  // 16-byte chunks per K/V row
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
-    constexpr float kTau = 8.0f; // deferred-rescale threshold (log2 units)
+    constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8: deferred-rescale threshold
     static_assert(BC * KCH == 2 * kThreads, "K and V tiles = two 16-byte chunks per thread each");
     // Three tile stages as separate LDS objects: the compiler can then tell
     // that the direct-to-LDS loads into one stage do not alias the reads of
@@ -237,19 +251,19 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int kv_end = CAUSAL ? min(N, q0 + kQueryBlock) : N;
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    // --- tile loader: direct global -> LDS loads ------------------------------
+    // --- tile loader: direct global -> LDS buffer loads -----------------------
     // Load j of wave w fills 1 KB block b = w + 8j of the stage: lane l writes
     // stage byte 1024 b + 16 l.  Blocks below NK hold the K tile (row pitch KP),
-    // the next NV the V tile (pitch VP), the rest are spare.  A lane whose slot
-    // falls in a row's padding re-reads the row's first chunk, a row at or past
-    // kv_end re-reads row kv_end-1 (its scores are masked, its weights 0), and a
-    // spare block re-reads the tile's first K row; none of these bytes is read
-    // back.  Every tile issues its loads unconditionally, also the two tiles
-    // past the last (they re-read row kv_end-1 into stages nobody reads again),
-    // so that each wave has exactly LPW loads in flight at every barrier.
+    // the next NV the V tile (pitch VP), the rest are spare.  The buffer
+    // descriptor of a tile starts at its first row and covers only its rows
+    // below kv_end, so rows past the end (and spare blocks, given an offset
+    // past any tile) read as zeros without touching memory; their scores are
+    // masked and their weights are 0.  A lane whose slot falls in a row's
+    // padding re-reads the row's first chunk; those bytes are never read back.
+    // Every tile issues its loads unconditionally, also the two tiles past the
+    // last, so that each wave has exactly LPW loads in flight at every barrier.
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
-    const uint16_t *src[LPW];
-    int srow[LPW];
+    uint32_t voff[LPW]; // byte offset of the lane's 16 bytes from the tile's first row
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int blk = wave + kWaves * j;
@@ -257,18 +271,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         const int pitch = is_k ? KP : VP;
         const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
         const int chunk = (pos % pitch) / 16;
-        const int off = chunk < KCH ? 8 * chunk : 0;
-        srow[j] = (is_k || is_v) ? pos / pitch : 0;
-        src[j] = (is_v ? V : K) + ((is_k || is_v) ? off : 0);
+        voff[j] = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u
+                                 : 0x40000000u;
     }
     auto issue_tile = [&](int t, lds_char *st) {
         const int k0 = t * BC;
+        const uint32_t bytes =
+            __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D * 2)); // uniform
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int key = min(k0 + srow[j], kv_end - 1);
-            __builtin_amdgcn_global_load_lds((const void *)(src[j] + (int64_t)key * D),
-                                             (__attribute__((address_space(3))) void *)(st + 1024 * (wave + kWaves * j)),
-                                             16, 0, 0);
+            const int blk = wave + kWaves * j; // wave-uniform
+            load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, voff[j],
+                        st + 1024 * (wave + kWaves * j));
         }
     };
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -332,35 +346,44 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                         s[kb][i] = vis ? s[kb][i] : -INFINITY;
                     }
             }
-            // online softmax: tile row maximum over the lane pair
-            float mx = -INFINITY;
+            // online softmax against the current reference m_ref:
+            // P~ = exp2(s*c - m_ref), summed in fp32, then rounded for the PV MFMA
+            uint32_t pk[KB][8];
+            float lt = 0.f;
+            auto exps = [&](float m_ref) {
+                lt = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s[kb][i]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m_run, mx * c);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
+                    for (int i = 0; i < 16; i += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
+                        lt += p0 + p1;
+                        pk[kb][i >> 1] = E::pack(p0, p1);
+                    }
+            };
+            exps(m_run == -INFINITY ? 0.f : m_run);
+            // The reference moves only when it is missing (first tile) or some
+            // row's share exceeds 2^kTau, i.e. a score beat the reference by
+            // more than kTau (log2 units); P~ <= 2^kTau keeps fp32 far from
+            // overflow.  Then rescale O and l to the row maximum and redo P~.
+            if (__builtin_amdgcn_ballot_w64(!(lt <= kLimit) || m_run == -INFINITY)) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        mx = fmaxf(mx, s[kb][i]);
+                const float m_new = fmaxf(m_run, pair_max(mx) * c);
                 const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
 #pragma unroll
                 for (int b = 0; b < OB; ++b)
                     o[b] *= alpha;
                 m_run = m_new;
+                exps(m_run == -INFINITY ? 0.f : m_run);
             }
-            const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-            // P~ = exp2(s*c - m), summed in fp32, then rounded for the PV MFMA
-            uint32_t pk[KB][8];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
-                    l_run += p0 + p1;
-                    pk[kb][i >> 1] = E::pack(p0, p1);
-                }
+            l_run += lt;
             // O^T += V^T P^T : o[b][i] accumulates feature 32b + 8(i/4) + 4g + i%4 of query qi
 #pragma unroll
             for (int b = 0; b < OB; ++b)
