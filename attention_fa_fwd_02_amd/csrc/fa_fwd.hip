@@ -202,7 +202,7 @@ struct F16 {
 // ----------------------------------------------------------------------------
 template <int D>
 struct MfmaCfg {
-    static constexpr int BC = (D == 64) ? 128 : 64; // keys per tile (K and V tiles are 16 KB each)
+    static constexpr int BC = 128;                  // keys per tile
     static constexpr int KP = 2 * D + 16;           // K row pitch in LDS (bytes)
     static constexpr int VP = 2 * D + 32;           // V row pitch in LDS (bytes)
     // tiles arrive by direct-to-LDS loads: one instruction fills 1 KB (64 lanes x
@@ -217,9 +217,8 @@ struct MfmaCfg {
     static constexpr int STAGE = 1024 * kWaves * LPW;
     static_assert(KST + BC * VP <= STAGE, "K and V regions fit in a stage");
     static constexpr int OP = 2 * D + 16;           // O staging row pitch (bytes)
-    static constexpr int STAGES = 3;
+    static constexpr int STAGES = 2;
     static constexpr int LDS = STAGES * STAGE;
-    static_assert(kWaves * 32 * OP <= LDS, "O staging fits in the tile buffers");
     static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
 };
 
@@ -233,16 +232,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr int KCH = D / 8;  // 16-byte chunks per K/V row
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
     constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8: deferred-rescale threshold
-    static_assert(BC * KCH == 2 * kThreads, "K and V tiles = two 16-byte chunks per thread each");
-    // Three tile stages as separate LDS objects: the compiler can then tell
-    // that the direct-to-LDS loads into one stage do not alias the reads of
-    // another, and does not wait for them before every LDS read.
+    // Two tile stages as separate LDS objects: the compiler can then tell that
+    // the direct-to-LDS loads into one stage do not alias the reads of the
+    // other, and does not wait for them before every LDS read.
     __shared__ __attribute__((aligned(16))) char stage0_raw[Cfg::STAGE];
     __shared__ __attribute__((aligned(16))) char stage1_raw[Cfg::STAGE];
-    __shared__ __attribute__((aligned(16))) char stage2_raw[Cfg::STAGE];
     lds_char *const stage0 = (lds_char *)stage0_raw;
     lds_char *const stage1 = (lds_char *)stage1_raw;
-    lds_char *const stage2 = (lds_char *)stage2_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -329,8 +325,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // one tile: issue the loads of tile t+2 into the stage tile t-1 used (free
     // since the last barrier), compute tile t from stage `cur`, then make tile
     // t+1 visible
-    auto tile = [&](int t, const lds_char *cur, lds_char *next2) {
-        issue_tile(t + 2, next2);
+    auto tile = [&](int t, const lds_char *cur, lds_char *next) {
+        issue_tile(t + 1, next);
         const int k0 = t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
         if (active) {
@@ -418,40 +414,28 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                         o[b] = E::mfma(vv, pb, o[b]);
                     }
         }
-        // this wave's loads of tile t+1 have landed once only those of tile t+2
-        // are in flight; the barrier then publishes tile t+1 to every wave
-        wait_vmcnt<LPW>();
+        // this wave's loads of tile t+1 have landed; the barrier then
+        // publishes tile t+1 to every wave
+        wait_vmcnt<0>();
         tile_barrier();
     };
 
-    // tiles 0 and 1 in flight; tile 0 complete before the first barrier
     issue_tile(0, stage0);
-    issue_tile(1, stage1);
-    wait_vmcnt<LPW>();
-    tile_barrier();
-    // tile t lives in stage t % 3.  Whole groups of three tiles run in the
-    // loop, with no exit between them, and the one or two left over after it:
-    // every access then names its stage object statically, and on every path
-    // into a tile only loads of the other two stages can still be in flight.
-    int t = 0;
-    for (; t + 3 <= n_tiles; t += 3) {
-        tile(t, stage0, stage2);
-        tile(t + 1, stage1, stage0);
-        tile(t + 2, stage2, stage1);
-    }
-    if (t < n_tiles) {
-        tile(t, stage0, stage2);
-        if (t + 1 < n_tiles)
-            tile(t + 1, stage1, stage0);
-    }
-    // the loads past the last tile must land before stages 0 and 1 are reused
     wait_vmcnt<0>();
     tile_barrier();
+    int t = 0;
+    for (; t + 2 <= n_tiles; t += 2) {
+        tile(t, stage0, stage1);
+        tile(t + 1, stage1, stage0);
+    }
+    if (t < n_tiles)
+        tile(t, stage0, stage1);
 
     // --- epilogue: O / l staged through LDS (wave-private rows), lse ---------
     const float l_tot = pair_sum(l_run);
     const float inv = 1.0f / l_tot;
     static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
+    tile_barrier();
     lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
     if (q0w < N) {
 #pragma unroll
