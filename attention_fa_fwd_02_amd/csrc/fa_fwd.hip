@@ -326,7 +326,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // since the last barrier), compute tile t from stage `cur`, then make tile
     // t+1 visible
     auto tile = [&](int t, const lds_char *cur, lds_char *next) {
-        issue_tile(t + 1, next);
         const int k0 = t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
         if (active) {
@@ -345,6 +344,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                     const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(ks + 32 * kb * KP + 32 * cc);
                     s[kb] = E::mfma(kv, qf[cc], s[kb]);
                 }
+            // schedule: four K reads ahead of the MFMAs, then one read per MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int n = 0; n < KB * DC - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            // the next tile's loads go out after the score phase, so their LDS
+            // writes do not land among its K reads
+            issue_tile(t + 1, next);
             // masking: keys beyond N, and keys after the query when causal
             if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
 #pragma unroll
@@ -413,6 +423,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                                           pk[kb][4 * mm + 3]};
                         o[b] = E::mfma(vv, pb, o[b]);
                     }
+        } else {
+            issue_tile(t + 1, next);
         }
         // this wave's loads of tile t+1 have landed; the barrier then
         // publishes tile t+1 to every wave
