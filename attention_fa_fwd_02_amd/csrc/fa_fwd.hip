@@ -382,12 +382,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                         pk[kb][i >> 1] = E::pack(p0, p1);
                     }
             };
-            exps(m_run == -INFINITY ? 0.f : m_run);
-            // The reference moves only when it is missing (first tile) or some
-            // row's share exceeds 2^kTau, i.e. a score beat the reference by
-            // more than kTau (log2 units); P~ <= 2^kTau keeps fp32 far from
-            // overflow.  Then rescale O and l to the row maximum and redo P~.
-            if (__builtin_amdgcn_ballot_w64(!(lt <= kLimit) || m_run == -INFINITY)) {
+            // The reference moves only when it is missing (first tile: no
+            // optimistic pass then) or some row's share exceeds 2^kTau, i.e. a
+            // score beat the reference by more than kTau (log2 units); P~ <=
+            // 2^kTau keeps fp32 far from overflow.  Then rescale O and l to the
+            // row maximum and redo P~.
+            bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+            if (!move) {
+                exps(m_run);
+                move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
+            }
+            if (move) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)

@@ -130,7 +130,7 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=12.0):
             "check_max_abs_dO": eo, "check_max_abs_dlse": el}
 
 
-def bench_one(name, steps, warmup, with_cpu, copy_calibration=False):
+def bench_one(name, steps, warmup, copy_calibration=False):
     import torch
 
     import attention_fa_fwd_02_amd as fa
@@ -186,9 +186,8 @@ def bench_one(name, steps, warmup, with_cpu, copy_calibration=False):
            100 * achieved / peak, dtype))
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
                kernel_ms=kern_ms, value=value, achieved=achieved, peak=peak, flops=flops)
-    if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(host, (o, lse), B, H, N, D, dtype, causal)
-    return res
+    # inputs and outputs stay alive for the CPU-oracle leg, which runs after all GPU timing
+    return res, (host, (o, lse), B, H, N, D, dtype, causal)
 
 
 def main():
@@ -212,14 +211,16 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    main_res = bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
-                         args.copy_calibration)
+    main_res, main_ctx = bench_one(args.workload, args.steps, args.warmup, args.copy_calibration)
     if args.all:
+        # every GPU timing comes before the CPU-oracle leg, whose minutes of host
+        # work would otherwise leave the GPU idle (and down-clocked) right before
         for name in WORKLOADS:
             if name != args.workload:
-                bench_one(name, max(3, args.steps // 5), 2, False)
-
+                bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     r = main_res
+    if not args.no_cpu_baseline:
+        r["cpu_baseline"] = cpu_baseline(*main_ctx)
     traffic = read_traffic() if r["name"] == "headline" else None
     out = {
         "metric": METRIC,
