@@ -266,14 +266,21 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // stage byte 1024 b + 16 l.  Blocks below NK hold the K tile (row pitch KP),
     // the next NV the V tile (pitch VP), the rest are spare.  The buffer
     // descriptor of a tile starts at its first row and covers only its rows
-    // below kv_end, so rows past the end (and spare blocks, given an offset
-    // past any tile) read as zeros without touching memory; their scores are
-    // masked and their weights are 0.  A lane whose slot falls in a row's
-    // padding re-reads the row's first chunk; those bytes are never read back.
-    // Every tile issues its loads unconditionally, also the two tiles past the
-    // last, so that each wave has exactly LPW loads in flight at every barrier.
+    // below kv_end, so rows past the end read as zeros without touching
+    // memory; their scores are masked and their weights are 0.  A lane whose
+    // slot falls in a row's padding re-reads the row's first chunk; those
+    // bytes are never read back.  Every tile issues the next tile's loads
+    // unconditionally, also past the last tile, so that every wave issues the
+    // same loads on every path.
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
-    uint32_t voff[LPW]; // byte offset of the lane's 16 bytes from the tile's first row
+    // byte offset of the lane's 16 bytes from the tile's first row, two 16-bit
+    // offsets per register (a tile is at most 32 KB); spare blocks read the
+    // first row again
+    static_assert(BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
+    uint32_t voff2[(LPW + 1) / 2];
+#pragma unroll
+    for (int j = 0; j < (LPW + 1) / 2; ++j)
+        voff2[j] = 0u;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int blk = wave + kWaves * j;
@@ -281,8 +288,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         const int pitch = is_k ? KP : VP;
         const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
         const int chunk = (pos % pitch) / 16;
-        voff[j] = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u
-                                 : 0x40000000u;
+        const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
+        voff2[j / 2] |= off << (16 * (j % 2));
     }
     auto issue_tile = [&](int t, lds_char *st) {
         const int k0 = t * BC;
@@ -291,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int blk = wave + kWaves * j; // wave-uniform
-            load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, voff[j],
+            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+            load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, off,
                         st + 1024 * (wave + kWaves * j));
         }
     };
