@@ -14,6 +14,9 @@ file's header for the passages it follows).  This module only
   * rounds the scale to the fp32 value a GPU caller passes
     (``float(np.float32(scale))``), and
   * loops over (batch, head) slices, handing each to the C routine.
+
+It also holds the merge of key-split partial results (``lse_merge``), in
+numpy fp64, written from the pages' online-softmax merge step.
 """
 from __future__ import annotations
 
@@ -51,6 +54,13 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.oracle_attention_rows_range.restype = ctypes.c_int
+        lib.oracle_attention_rows_range.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -85,9 +95,14 @@ def gpu_scale(scale: float) -> float:
     return float(np.float32(scale))
 
 
-def attention_rows(q_rows, k, v, rows, scale: float, causal: bool, n_threads: int = 0):
+def attention_rows(q_rows, k, v, rows, scale: float, causal: bool, n_threads: int = 0,
+                   key_range=None):
     """One [N, D] slice: outputs (O_rows [R, D], lse_rows [R]) in fp64 for the query
-    positions ``rows`` (q_rows[r] is query rows[r]).  All arrays are float64."""
+    positions ``rows`` (q_rows[r] is query rows[r]).  All arrays are float64.
+
+    ``key_range = (lo, hi)`` restricts the keys to lo <= j < hi (the partial
+    result of one key split); a row with no visible key gets lse = -inf and
+    O = 0."""
     lib = _load()
     q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -99,18 +114,20 @@ def attention_rows(q_rows, k, v, rows, scale: float, causal: bool, n_threads: in
                          % (q_rows.shape, k.shape, v.shape, rows.shape))
     o = np.empty((rows.shape[0], d), dtype=np.float64)
     lse = np.empty((rows.shape[0],), dtype=np.float64)
-    rc = lib.oracle_attention_rows(
+    lo, hi = (0, n_keys) if key_range is None else (int(key_range[0]), int(key_range[1]))
+    rc = lib.oracle_attention_rows_range(
         q_rows.ctypes.data, k.ctypes.data, v.ctypes.data, n_keys, d,
-        rows.ctypes.data, rows.shape[0], float(scale), int(bool(causal)),
+        rows.ctypes.data, rows.shape[0], lo, hi, float(scale), int(bool(causal)),
         o.ctypes.data, lse.ctypes.data, int(n_threads))
     if rc != 0:
         raise ValueError("oracle_attention_rows failed with code %d" % rc)
     return o, lse
 
 
-def attention(q, k, v, scale: float, causal: bool, n_threads: int = 0):
+def attention(q, k, v, scale: float, causal: bool, n_threads: int = 0, key_range=None):
     """Full [..., N, D] tensors in fp64 (leading dims are independent slices).
-    Returns (O [..., N, D], lse [..., N]) in fp64."""
+    Returns (O [..., N, D], lse [..., N]) in fp64.  ``key_range`` as in
+    ``attention_rows``."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -123,5 +140,42 @@ def attention(q, k, v, scale: float, causal: bool, n_threads: int = 0):
     lse = np.empty(qf.shape[:2], dtype=np.float64)
     rows = np.arange(n, dtype=np.int64)
     for s in range(qf.shape[0]):
-        o[s], lse[s] = attention_rows(qf[s], kf[s], vf[s], rows, scale, causal, n_threads)
+        o[s], lse[s] = attention_rows(qf[s], kf[s], vf[s], rows, scale, causal, n_threads,
+                                      key_range)
     return o.reshape(*lead, n, d), lse.reshape(*lead, n)
+
+
+def lse_merge(part_o, part_lse):
+    """Merge partial results over disjoint key sets into the result over their union.
+
+    part_o [P, ..., D] and part_lse [P, ...] (fp64): part p is the normalised
+    output O_p and logsumexp lse_p of the same query rows over key set p.
+    This is the online-softmax merge of a running state with a new block's
+    statistics (KingOfEgg's FlashAttention v1 post, section 4.3, the
+    m_new / l_new / O update), applied to P parts at once.  A part's
+    (m_p, l_p) pair enters only through lse_p = m_p + ln l_p, so each part
+    is taken with m_p = lse_p and l_p = 1:
+
+        m   = max_p lse_p
+        w_p = exp(lse_p - m)          (the exp(m_old - m_new) factors)
+        l   = sum_p w_p
+        O   = sum_p w_p O_p / l
+        lse = m + ln l
+
+    A part with lse_p = -inf (no visible key) has weight 0 and its O_p is
+    not read.  A row whose parts are all -inf gets lse = -inf and O = 0.
+    Returns (O [..., D], lse [...]) in fp64.
+    """
+    part_o = np.asarray(part_o, dtype=np.float64)
+    part_lse = np.asarray(part_lse, dtype=np.float64)
+    if part_o.shape[:-1] != part_lse.shape or part_lse.ndim < 1 or part_lse.shape[0] < 1:
+        raise ValueError("part_o %s and part_lse %s do not match" % (part_o.shape, part_lse.shape))
+    m = part_lse.max(axis=0)
+    empty = m == -np.inf
+    m_safe = np.where(empty, 0.0, m)
+    w = np.where(part_lse == -np.inf, 0.0, np.exp(part_lse - m_safe))
+    l = w.sum(axis=0)
+    contrib = np.where((w > 0)[..., None], w[..., None] * np.nan_to_num(part_o), 0.0)
+    o = np.where(empty[..., None], 0.0, contrib.sum(axis=0) / np.where(empty, 1.0, l)[..., None])
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return o, lse

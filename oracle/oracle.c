@@ -19,6 +19,10 @@
  * with J(i) = {0..N-1} (non-causal) or {0..i} (causal, key j > query i
  * masked, top-left aligned).
  *
+ * The same definition over a key range [lo, hi) (J(i) intersected with it)
+ * gives the partial result of one key split.  An empty J(i) gives the empty
+ * sum: l_i = 0, m_i = -inf, lse_i = ln 0 = -inf, O_i = 0.
+ *
  * Sources (pages on the FlashAttention forward pass):
  *   - the three-line definition S = QK^T/sqrt(d_k), P = softmax(S), O = PV
  *     and the statement that each row of P is a probability distribution:
@@ -58,25 +62,29 @@ int oracle_default_threads(void)
 }
 
 /*
- * One (batch, head) slice.
+ * One (batch, head) slice, keys restricted to [key_lo, key_hi).
  *   q_rows    [n_rows, d]   the query rows to evaluate (row r is query index row_index[r])
  *   k, v      [n_keys, d]   all keys and values of the slice
  *   row_index [n_rows]      query position of each row (0 <= row_index[r] < n_keys)
+ *   key_lo, key_hi          key range, 0 <= key_lo <= key_hi <= n_keys
  *   scale                   multiplies every dot product
- *   causal                  0: all keys; 1: keys 0..row_index[r]
+ *   causal                  0: keys of the range; 1: those up to row_index[r]
  *   o_rows    [n_rows, d]   output rows (fp64)
  *   lse_rows  [n_rows]      natural-log logsumexp of the scaled scores (fp64)
  *   n_threads               OpenMP threads (<= 0: the runtime default)
  * Returns 0 on success, 1 on an invalid argument, 2 if memory ran out.
  */
-int oracle_attention_rows(const double *q_rows, const double *k, const double *v,
-                          int64_t n_keys, int64_t d, const int64_t *row_index,
-                          int64_t n_rows, double scale, int causal,
-                          double *o_rows, double *lse_rows, int n_threads)
+int oracle_attention_rows_range(const double *q_rows, const double *k, const double *v,
+                                int64_t n_keys, int64_t d, const int64_t *row_index,
+                                int64_t n_rows, int64_t key_lo, int64_t key_hi,
+                                double scale, int causal, double *o_rows, double *lse_rows,
+                                int n_threads)
 {
     if (!q_rows || !k || !v || !row_index || !o_rows || !lse_rows)
         return 1;
     if (n_keys < 1 || d < 1 || n_rows < 0 || (causal != 0 && causal != 1))
+        return 1;
+    if (key_lo < 0 || key_hi < key_lo || key_hi > n_keys)
         return 1;
     for (int64_t r = 0; r < n_rows; r++)
         if (row_index[r] < 0 || row_index[r] >= n_keys)
@@ -102,41 +110,52 @@ int oracle_attention_rows(const double *q_rows, const double *k, const double *v
             const int64_t i = row_index[r];
             const double *qi = q_rows + r * d;
             double *oi = o_rows + r * d;
-            /* key set J(i) */
-            const int64_t n_vis = causal ? i + 1 : n_keys;
+            /* key set J(i) = [key_lo, j_end); S[j - key_lo] holds key j */
+            const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;
 
             /* explicit score row: dot product first, then the scale */
-            for (int64_t j = 0; j < n_vis; j++) {
+            for (int64_t j = key_lo; j < j_end; j++) {
                 const double *kj = k + j * d;
                 double dot = 0.0;
                 for (int64_t c = 0; c < d; c++)
                     dot += qi[c] * kj[c];
-                S[j] = scale * dot;
+                S[j - key_lo] = scale * dot;
             }
             /* pass 1: row maximum */
             double m = -INFINITY;
-            for (int64_t j = 0; j < n_vis; j++)
-                if (S[j] > m)
-                    m = S[j];
+            for (int64_t j = key_lo; j < j_end; j++)
+                if (S[j - key_lo] > m)
+                    m = S[j - key_lo];
             /* pass 2: sum of exp(S - m) */
             double l = 0.0;
-            for (int64_t j = 0; j < n_vis; j++)
-                l += exp(S[j] - m);
+            for (int64_t j = key_lo; j < j_end; j++)
+                l += exp(S[j - key_lo] - m);
             /* pass 3: normalised probabilities, kept in place of S */
-            for (int64_t j = 0; j < n_vis; j++)
-                S[j] = exp(S[j] - m) / l;
+            for (int64_t j = key_lo; j < j_end; j++)
+                S[j - key_lo] = exp(S[j - key_lo] - m) / l;
             /* O = P V */
             for (int64_t c = 0; c < d; c++)
                 oi[c] = 0.0;
-            for (int64_t j = 0; j < n_vis; j++) {
-                const double p = S[j];
+            for (int64_t j = key_lo; j < j_end; j++) {
+                const double p = S[j - key_lo];
                 const double *vj = v + j * d;
                 for (int64_t c = 0; c < d; c++)
                     oi[c] += p * vj[c];
             }
+            /* an empty key set leaves m = -inf and l = 0: lse = -inf, O = 0 */
             lse_rows[r] = m + log(l);
         }
         free(S);
     }
     return failed ? 2 : 0;
+}
+
+/* The whole key range: softmax(scale * q k^T) v over J(i). */
+int oracle_attention_rows(const double *q_rows, const double *k, const double *v,
+                          int64_t n_keys, int64_t d, const int64_t *row_index,
+                          int64_t n_rows, double scale, int causal,
+                          double *o_rows, double *lse_rows, int n_threads)
+{
+    return oracle_attention_rows_range(q_rows, k, v, n_keys, d, row_index, n_rows, 0, n_keys,
+                                       scale, causal, o_rows, lse_rows, n_threads);
 }

@@ -34,17 +34,20 @@ def test_oracle_passes_pin(pin):
 _SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTATIONS = {
-    "scale_dropped": [("S[j] = scale * dot;", "S[j] = dot;")],
+    "scale_dropped": [("S[j - key_lo] = scale * dot;", "S[j - key_lo] = dot;")],
     "feature_index_reversed": [("dot += qi[c] * kj[c];", "dot += qi[c] * kj[d - 1 - c];")],
     "dot_term_dropped": [("for (int64_t c = 0; c < d; c++)\n                    dot",
                           "for (int64_t c = 0; c < d - 1; c++)\n                    dot")],
-    "exp_sign_flipped": [("l += exp(S[j] - m);", "l += exp(m - S[j]);"),
-                         ("S[j] = exp(S[j] - m) / l;", "S[j] = exp(m - S[j]) / l;")],
-    "not_normalised": [("S[j] = exp(S[j] - m) / l;", "S[j] = exp(S[j] - m);")],
-    "value_row_reversed": [("const double *vj = v + j * d;", "const double *vj = v + (n_vis - 1 - j) * d;")],
+    "exp_sign_flipped": [("l += exp(S[j - key_lo] - m);", "l += exp(m - S[j - key_lo]);"),
+                         ("S[j - key_lo] = exp(S[j - key_lo] - m) / l;",
+                          "S[j - key_lo] = exp(m - S[j - key_lo]) / l;")],
+    "not_normalised": [("S[j - key_lo] = exp(S[j - key_lo] - m) / l;",
+                        "S[j - key_lo] = exp(S[j - key_lo] - m);")],
+    "value_row_reversed": [("const double *vj = v + j * d;",
+                            "const double *vj = v + (j_end - 1 - j + key_lo) * d;")],
     "value_column_shifted": [("oi[c] += p * vj[c];", "oi[c] += p * vj[(c + 1) % d];")],
-    "causal_sees_next_key": [("const int64_t n_vis = causal ? i + 1 : n_keys;",
-                              "const int64_t n_vis = causal ? (i + 2 < n_keys ? i + 2 : n_keys) : n_keys;")],
+    "causal_sees_next_key": [("const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;",
+                              "const int64_t j_end = causal ? (i + 2 < key_hi ? i + 2 : key_hi) : key_hi;")],
     "lse_in_log2": [("lse_rows[r] = m + log(l);", "lse_rows[r] = m + log2(l);")],
     "lse_without_max": [("lse_rows[r] = m + log(l);", "lse_rows[r] = log(l);")],
 }
