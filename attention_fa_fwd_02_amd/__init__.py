@@ -5,9 +5,12 @@ of the computation runs in the HIP kernels of ``libfa.so``; this module only
 marshals arguments.  There is no fallback: if the library is missing or the
 device is not gfx950 the calls raise.
 
-Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_status_string``,
-``fa_abi_version``.  ``fwd`` is a convenience wrapper that allocates O and lse
-with torch (device memory and the current stream are all torch provides).
+Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
+``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
+``fa_status_string``, ``fa_abi_version``.  ``fwd``, ``fwd_split`` and
+``lse_merge`` are convenience wrappers that allocate outputs (and the split
+workspace) with torch (device memory and the current stream are all torch
+provides).
 """
 from __future__ import annotations
 
@@ -16,11 +19,14 @@ import math
 import os
 
 __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INVALID_ARG",
-           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FaError", "lib_path", "load_library", "fa_fwd",
-           "fa_check_args", "fa_status_string", "fa_abi_version", "fwd"]
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_MAX_SPLITS", "FaError", "lib_path",
+           "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
+           "fa_fwd_split_choose", "fa_lse_merge", "fa_status_string", "fa_abi_version",
+           "fwd", "fwd_split", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_MAX_SPLITS = 64
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -52,6 +58,15 @@ def load_library():
         lib.fa_check_args.restype = ctypes.c_int
         lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_char_p]
+        lib.fa_fwd_split.restype = ctypes.c_int
+        lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                     ctypes.c_int, ctypes.c_int, i64, vp, ctypes.c_uint64, vp]
+        lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_uint64
+        lib.fa_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        lib.fa_fwd_split_choose.restype = i64
+        lib.fa_fwd_split_choose.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64]
+        lib.fa_lse_merge.restype = ctypes.c_int
+        lib.fa_lse_merge.argtypes = [vp, vp, i64, i64, i64, vp, vp, ctypes.c_int, vp]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -79,6 +94,30 @@ def fa_check_args(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: i
     """Host-only argument check (no HIP call); returns the fa_status code."""
     a = arch.encode() if arch is not None else None
     return int(load_library().fa_check_args(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, a))
+
+
+def fa_fwd_split(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int,
+                 scale: float, causal: int, dtype: int, n_splits: int, workspace: int,
+                 workspace_bytes: int, stream: int) -> int:
+    """Raw C call with integer device addresses; returns the fa_status code."""
+    return int(load_library().fa_fwd_split(q, k, v, o, lse, B, H, N, D, scale, causal, dtype,
+                                           n_splits, workspace, workspace_bytes, stream))
+
+
+def fa_fwd_split_workspace_bytes(B: int, H: int, N: int, D: int, n_splits: int) -> int:
+    """Workspace bytes fa_fwd_split needs (0 for invalid arguments); host only."""
+    return int(load_library().fa_fwd_split_workspace_bytes(B, H, N, D, n_splits))
+
+
+def fa_fwd_split_choose(B: int, H: int, N: int, D: int, causal: int, n_cus: int) -> int:
+    """The library's split count for a device with n_cus compute units; host only."""
+    return int(load_library().fa_fwd_split_choose(B, H, N, D, int(causal), n_cus))
+
+
+def fa_lse_merge(part_o: int, part_lse: int, n_parts: int, rows: int, D: int, o: int, lse: int,
+                 dtype: int, stream: int) -> int:
+    """Raw C call with integer device addresses; returns the fa_status code."""
+    return int(load_library().fa_lse_merge(part_o, part_lse, n_parts, rows, D, o, lse, dtype, stream))
 
 
 def _dtype_code(t) -> int:
@@ -121,4 +160,83 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
                     B, H, N, D, float(scale), int(bool(causal)), _dtype_code(q.dtype), handle)
     if st != FA_OK:
         raise FaError(st)
+    return out, lse
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, n_splits: int | None = None,
+              out=None, lse=None, workspace=None, stream=None):
+    """``fwd`` computed as key splits merged on the device (fa_fwd_split).
+
+    n_splits defaults to fa_fwd_split_choose for the device's compute-unit
+    count.  ``workspace`` (a uint8 CUDA tensor of at least
+    fa_fwd_split_workspace_bytes bytes) is allocated when not given.
+    Returns (O, lse, workspace); the workspace holds the per-split fp32
+    outputs [n_splits, B, H, N, D] followed by their lse [n_splits, B, H, N].
+    """
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, D] with the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s is not a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous [B, H, N, D]" % name)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if n_splits is None:
+        n_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        n_splits = fa_fwd_split_choose(B, H, N, D, int(bool(causal)), n_cus)
+    need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, D, float(scale), int(bool(causal)), _dtype_code(q.dtype), n_splits,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(), handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
+    return out, lse, workspace
+
+
+def lse_merge(part_o, part_lse, out_dtype=None, out=None, lse=None, stream=None):
+    """Merge partial results: part_o fp32 [P, ..., D], part_lse fp32 [P, ...] (CUDA,
+    contiguous) -> (O [..., D] of out_dtype (default float32), lse [...] fp32)."""
+    import torch
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("part_o and part_lse must be float32")
+    if part_o.dim() < 2 or tuple(part_o.shape[:-1]) != tuple(part_lse.shape):
+        raise ValueError("part_o [P, ..., D] and part_lse [P, ...] do not match")
+    for name, t in (("part_o", part_o), ("part_lse", part_lse)):
+        if not t.is_cuda:
+            raise ValueError("%s is not a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    P, D = part_o.shape[0], part_o.shape[-1]
+    rows = part_lse.numel() // P
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(part_o.shape[1:], dtype=out_dtype, device=part_o.device)
+    if lse is None:
+        lse = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_o.device)
+    handle = _stream_handle(stream, part_o.device)
+    with torch.cuda.device(part_o.device):
+        st = fa_lse_merge(part_o.data_ptr(), part_lse.data_ptr(), P, rows, D, out.data_ptr(),
+                          lse.data_ptr(), _dtype_code(out.dtype), handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_lse_merge")
     return out, lse

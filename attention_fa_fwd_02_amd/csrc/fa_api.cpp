@@ -4,6 +4,7 @@
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -22,6 +23,59 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// Current device must be gfx950 (cached per device after the first query).
+fa_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return FA_ERR_HIP;
+    std::call_once(g_arch_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        g_arch_err[dev] = hipGetDeviceProperties(&prop, dev);
+        if (g_arch_err[dev] == hipSuccess) {
+            std::strncpy(g_arch[dev], prop.gcnArchName, sizeof(g_arch[dev]) - 1);
+            g_arch[dev][sizeof(g_arch[dev]) - 1] = '\0';
+        }
+    });
+    if (g_arch_err[dev] != hipSuccess)
+        return FA_ERR_HIP;
+    if (std::strncmp(g_arch[dev], "gfx950", 6) != 0)
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse, int64_t N,
+                      float scale, fa_dtype dtype) {
+    fa::FwdArgs args{};
+    args.q = q;
+    args.k = k;
+    args.v = v;
+    args.o = o;
+    args.lse = lse;
+    args.N = (int32_t)N;
+    args.n_qblk = (int32_t)((N + fa::kQueryBlock - 1) / fa::kQueryBlock);
+    const float log2e = 1.44269504088896340736f;
+    // c > 0 always: for |scale| * log2(e) below 1e-30 every weight exp2(c*s - m) is
+    // exactly 1.0f, the same as for scale = 0, and masked scores (-inf) give
+    // exp2(-inf) = 0 instead of the NaN that -inf * 0 would produce
+    args.c = std::fmax(std::fabs(scale) * log2e, 1e-30f);
+    args.qneg = std::signbit(scale) ? (dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u) : 0u;
+    return args;
+}
+
+// Keys per split: whole 128-key tiles, ceil(tiles / n_splits) of them.
+constexpr int64_t kSplitTile = 128;
+int64_t split_keys(int64_t N, int64_t n_splits) {
+    const int64_t tiles = (N + kSplitTile - 1) / kSplitTile;
+    return kSplitTile * ((tiles + n_splits - 1) / n_splits);
+}
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) {
+    if (a != 0 && b > UINT64_MAX / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
 } // namespace
 
 extern "C" {
@@ -36,8 +90,9 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim not 64/128, problem too large for one launch, or device is "
-               "not gfx950)";
+        return "unsupported (head dim not 64/128, problem too large for one launch, too many "
+               "key splits or merge parts, merge head dim not a power of two in 8..512, or device "
+               "is not gfx950)";
     case FA_ERR_HIP:
         return "HIP runtime error (device query or kernel launch failed)";
     default:
@@ -92,38 +147,111 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     fa_status st = fa_check_args(q, k, v, o, lse, B, H, N, D, scale, causal, (int)dtype, nullptr);
     if (st != FA_OK)
         return st;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return FA_ERR_HIP;
-    std::call_once(g_arch_once[dev], [dev] {
-        hipDeviceProp_t prop;
-        g_arch_err[dev] = hipGetDeviceProperties(&prop, dev);
-        if (g_arch_err[dev] == hipSuccess) {
-            std::strncpy(g_arch[dev], prop.gcnArchName, sizeof(g_arch[dev]) - 1);
-            g_arch[dev][sizeof(g_arch[dev]) - 1] = '\0';
-        }
-    });
-    if (g_arch_err[dev] != hipSuccess)
-        return FA_ERR_HIP;
-    if (std::strncmp(g_arch[dev], "gfx950", 6) != 0)
-        return FA_ERR_UNSUPPORTED;
-
-    fa::FwdArgs args;
-    args.q = q;
-    args.k = k;
-    args.v = v;
-    args.o = o;
-    args.lse = lse;
-    args.N = (int32_t)N;
-    args.n_qblk = (int32_t)((N + fa::kQueryBlock - 1) / fa::kQueryBlock);
-    const float log2e = 1.44269504088896340736f;
-    // c > 0 always: for |scale| * log2(e) below 1e-30 every weight exp2(c*s - m) is
-    // exactly 1.0f, the same as for scale = 0, and masked scores (-inf) give
-    // exp2(-inf) = 0 instead of the NaN that -inf * 0 would produce
-    args.c = std::fmax(std::fabs(scale) * log2e, 1e-30f);
-    args.qneg = std::signbit(scale) ? (dtype == FA_DTYPE_F32 ? 0x80000000u : 0x80008000u) : 0u;
-    const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, B * H, args,
+    if ((st = check_device()) != FA_OK)
+        return st;
+    const fa::FwdArgs args = make_args(q, k, v, o, lse, N, scale, dtype);
+    const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, false, B * H, args,
                                           reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+uint64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_splits) {
+    if (B < 1 || H < 1 || N < 1 || D < 1 || n_splits < 1)
+        return 0;
+    uint64_t x = 0;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &x) || !mul_ok(x, (uint64_t)N, &x) ||
+        !mul_ok(x, (uint64_t)D + 1u, &x) || !mul_ok(x, (uint64_t)n_splits, &x) || !mul_ok(x, 4u, &x))
+        return 0;
+    return x;
+}
+
+int64_t fa_fwd_split_choose(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int64_t n_cus) {
+    if (B < 1 || H < 1 || N < 1 || D < 1 || n_cus < 1 || (causal != 0 && causal != 1))
+        return 0;
+    const uint64_t n_qblk = ((uint64_t)N + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    uint64_t wgs = 0;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &wgs) || !mul_ok(wgs, n_qblk, &wgs) || wgs >= (uint64_t)n_cus)
+        return 1; // the grid already has a workgroup for every compute unit
+    int64_t s = (int64_t)(((uint64_t)n_cus + wgs - 1) / wgs);
+    // each split keeps >= 8 key tiles: a split's partial costs 8 bytes per row
+    // and feature (fp32 written, then read by the merge) against 4 flops per
+    // row, feature and key, so 1024 keys per split keep that round trip small
+    // next to the split's MFMA work
+    const int64_t tiles = (N + kSplitTile - 1) / kSplitTile;
+    s = std::min(s, tiles / 8);
+    s = std::min<int64_t>(s, FA_MAX_SPLITS);
+    return std::max<int64_t>(s, 1);
+}
+
+fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                       int64_t H, int64_t N, int64_t D, float scale, int causal, fa_dtype dtype,
+                       int64_t n_splits, void *workspace, uint64_t workspace_bytes,
+                       fa_stream_t stream) {
+    fa_status st = fa_check_args(q, k, v, o, lse, B, H, N, D, scale, causal, (int)dtype, nullptr);
+    if (st != FA_OK)
+        return st;
+    if (n_splits < 1 || !workspace || ((uintptr_t)workspace & 15u))
+        return FA_ERR_INVALID_ARG;
+    if (n_splits > FA_MAX_SPLITS)
+        return FA_ERR_UNSUPPORTED;
+    const uint64_t need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits);
+    if (need == 0 || workspace_bytes < need)
+        return FA_ERR_INVALID_ARG;
+    const int64_t BH = B * H;
+    const uint64_t tbytes = (uint64_t)(BH * N * D) * elem_size(dtype);
+    const uint64_t lbytes = (uint64_t)(BH * N) * 4u;
+    if (overlaps(workspace, need, q, tbytes) || overlaps(workspace, need, k, tbytes) ||
+        overlaps(workspace, need, v, tbytes) || overlaps(workspace, need, o, tbytes) ||
+        overlaps(workspace, need, lse, lbytes))
+        return FA_ERR_INVALID_ARG;
+    const int64_t n_qblk = (N + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    if (BH * n_qblk * n_splits >= (int64_t(1) << 23))
+        return FA_ERR_UNSUPPORTED;
+    if ((st = check_device()) != FA_OK)
+        return st;
+
+    fa::FwdArgs args = make_args(q, k, v, o, lse, N, scale, dtype);
+    const int64_t rows = BH * N;
+    args.part_o = (float *)workspace;
+    args.part_lse = (float *)((char *)workspace + (uint64_t)n_splits * (uint64_t)rows * (uint64_t)D * 4u);
+    args.part_rows = rows;
+    args.split_keys = (int32_t)split_keys(N, n_splits);
+    args.n_splits = (int32_t)n_splits;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, true, BH, args, hs);
+    if (err == hipSuccess)
+        err = fa::launch_merge((int)dtype, args.part_o, args.part_lse, (int)n_splits, rows, (int)D, o,
+                               lse, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_lse_merge(const float *part_o, const float *part_lse, int64_t n_parts, int64_t rows,
+                       int64_t D, void *o, float *lse, fa_dtype dtype, fa_stream_t stream) {
+    if (!part_o || !part_lse || !o || !lse)
+        return FA_ERR_INVALID_ARG;
+    if (n_parts < 1 || rows < 1 || D < 1)
+        return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
+    if ((((uintptr_t)part_o | (uintptr_t)o) & 15u) || (((uintptr_t)part_lse | (uintptr_t)lse) & 3u))
+        return FA_ERR_INVALID_ARG;
+    if (n_parts > 1024 || D < 8 || D > 512 || (D & (D - 1)) != 0)
+        return FA_ERR_UNSUPPORTED;
+    if (rows >= (int64_t(1) << 40) || n_parts * rows * D >= (int64_t(1) << 40))
+        return FA_ERR_UNSUPPORTED;
+    const uint64_t pobytes = (uint64_t)(n_parts * rows * D) * 4u;
+    const uint64_t plbytes = (uint64_t)(n_parts * rows) * 4u;
+    const uint64_t obytes = (uint64_t)(rows * D) * elem_size(dtype);
+    const uint64_t lbytes = (uint64_t)rows * 4u;
+    if (overlaps(o, obytes, lse, lbytes) || overlaps(o, obytes, part_o, pobytes) ||
+        overlaps(o, obytes, part_lse, plbytes) || overlaps(lse, lbytes, part_o, pobytes) ||
+        overlaps(lse, lbytes, part_lse, plbytes))
+        return FA_ERR_INVALID_ARG;
+    fa_status st = check_device();
+    if (st != FA_OK)
+        return st;
+    const hipError_t err = fa::launch_merge((int)dtype, part_o, part_lse, (int)n_parts, rows, (int)D, o,
+                                            lse, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

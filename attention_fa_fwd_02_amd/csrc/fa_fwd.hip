@@ -222,7 +222,7 @@ struct MfmaCfg {
     static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
 };
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     using Cfg = MfmaCfg<D>;
     constexpr int BC = Cfg::BC;
@@ -248,18 +248,34 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int N = a.N;
 
     const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
-    const int64_t slice = (int64_t)wk.bh * N * D;
+    // a key-split grid has n_splits rows per slice: (slice, split) = divmod(row)
+    const int bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
+    const int split = SPLIT ? wk.bh - bh * a.n_splits : 0;
+    const int64_t slice = (int64_t)bh * N * D;
     const uint16_t *__restrict__ Q = (const uint16_t *)a.q + slice;
     const uint16_t *__restrict__ K = (const uint16_t *)a.k + slice;
     const uint16_t *__restrict__ V = (const uint16_t *)a.v + slice;
     uint16_t *__restrict__ O = (uint16_t *)a.o + slice;
-    float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
+    float *__restrict__ LSE = a.lse + (int64_t)bh * N;
 
     const int q0 = wk.qb * kQueryBlock;
     const int q0w = q0 + 32 * wave; // first query row of this wave
     const int qi = q0w + r;         // this lane's query row
-    const int kv_end = CAUSAL ? min(N, q0 + kQueryBlock) : N;
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    // keys [k_begin, kv_end): the split's range (whole key tiles) cut at the
+    // last key any row of the block sees
+    const int k_begin = SPLIT ? split * a.split_keys : 0;
+    const int kv_vis = CAUSAL ? min(N, q0 + kQueryBlock) : N;
+    const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
+    const int n_tiles = SPLIT ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
+                              : (kv_end + BC - 1) / BC;
+    if constexpr (SPLIT) {
+        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * N;
+        if (n_tiles == 0) { // no key of this split is visible to the block
+            if (tid < kQueryBlock && q0 + tid < N)
+                PLSE[q0 + tid] = -INFINITY;
+            return;
+        }
+    }
 
     // --- tile loader: direct global -> LDS buffer loads -----------------------
     // Load j of wave w fills 1 KB block b = w + 8j of the stage: lane l writes
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         voff2[j / 2] |= off << (16 * (j % 2));
     }
     auto issue_tile = [&](int t, lds_char *st) {
-        const int k0 = t * BC;
+        const int k0 = k_begin + t * BC;
         const uint32_t bytes =
             __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D * 2)); // uniform
 #pragma unroll
@@ -334,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // since the last barrier), compute tile t from stage `cur`, then make tile
     // t+1 visible
     auto tile = [&](int t, const lds_char *cur, lds_char *next) {
-        const int k0 = t * BC;
+        const int k0 = k_begin + t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
         if (active) {
             const lds_char *ks = cur + k_lane;
@@ -458,6 +474,43 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
 
     // --- epilogue: O / l staged through LDS (wave-private rows), lse ---------
     const float l_tot = pair_sum(l_run);
+    if constexpr (SPLIT) {
+        // fp32 partial output; a row that sees no key of the split has l = 0
+        // and m = -inf: O = 0, lse = -inf
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
+        static_assert(4 * 32 * OP4 <= Cfg::STAGE, "four waves' fp32 O rows fit in one stage");
+        float *__restrict__ PO = a.part_o + (split * a.part_rows + (int64_t)bh * N) * D;
+        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * N;
+        tile_barrier();
+        lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4;
+        if (q0w < N) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
+                                     o[b][4 * a4 + 3] * inv};
+                    *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
+                }
+            if (g == 0 && qi < N)
+                PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        }
+        __syncthreads();
+        if (q0w < N) {
+            constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
+#pragma unroll
+            for (int j = 0; j < kChunks / 64; ++j) {
+                const int ch = 64 * j + lane;
+                const int row = ch / (D / 4), col = ch % (D / 4);
+                const int q = q0w + row;
+                const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
+                if (q < N)
+                    *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
+            }
+        }
+        return;
+    }
     const float inv = 1.0f / l_tot;
     static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
     tile_barrier();
@@ -501,7 +554,7 @@ struct F32Cfg {
     static constexpr int LDS = 2 * STAGE;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     using Cfg = F32Cfg<D>;
     constexpr int BC = Cfg::BC;
@@ -521,18 +574,31 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     const int N = a.N;
 
     const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
-    const int64_t slice = (int64_t)wk.bh * N * D;
+    const int bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
+    const int split = SPLIT ? wk.bh - bh * a.n_splits : 0;
+    const int64_t slice = (int64_t)bh * N * D;
     const float *__restrict__ Q = (const float *)a.q + slice;
     const float *__restrict__ K = (const float *)a.k + slice;
     const float *__restrict__ V = (const float *)a.v + slice;
-    float *__restrict__ O = (float *)a.o + slice;
-    float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
+    // a key split writes its normalised fp32 partial in place of O and lse
+    float *__restrict__ O = SPLIT ? a.part_o + (split * a.part_rows + (int64_t)bh * N) * D
+                                  : (float *)a.o + slice;
+    float *__restrict__ LSE = SPLIT ? a.part_lse + split * a.part_rows + (int64_t)bh * N
+                                    : a.lse + (int64_t)bh * N;
 
     const int q0 = wk.qb * kQueryBlock;
     const int q0w = q0 + 32 * wave;
     const int qi = q0w + r;
-    const int kv_end = CAUSAL ? min(N, q0 + kQueryBlock) : N;
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    const int k_begin = SPLIT ? split * a.split_keys : 0;
+    const int kv_vis = CAUSAL ? min(N, q0 + kQueryBlock) : N;
+    const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
+    const int n_tiles = SPLIT ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
+                              : (kv_end + BC - 1) / BC;
+    if (SPLIT && n_tiles == 0) { // no key of this split is visible to the block
+        if (tid < kQueryBlock && q0 + tid < N)
+            LSE[q0 + tid] = -INFINITY;
+        return;
+    }
 
     int ckey[NCH], ccol[NCH];
 #pragma unroll
@@ -544,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     f32x4 kr[NCH], vr[NCH];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     auto load_tile = [&](int t) {
-        const int k0 = t * BC;
+        const int k0 = k_begin + t * BC;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int key = k0 + ckey[i];
@@ -593,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         const int stage = t & 1;
         if (t + 1 < n_tiles)
             load_tile(t + 1);
-        const int k0 = t * BC;
+        const int k0 = k_begin + t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
         if (active) {
             const float *ks = (const float *)(smem + stage * Cfg::STAGE);
@@ -649,7 +715,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
 
     if (q0w < N) {
         const float l_tot = pair_sum(l_run);
-        const float inv = 1.0f / l_tot;
+        // a split row that sees no key: l = 0, m = -inf -> O = 0, lse = -inf
+        const float inv = (SPLIT && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
         if (qi < N) {
             float *orow = O + (int64_t)qi * D + 16 * g;
 #pragma unroll
@@ -669,54 +736,67 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
 
 constexpr int kMaxDevices = 64;
 
-// Dynamic LDS above 64 KB must be allowed per kernel; done once per device.
-template <typename KernelFn>
-hipError_t launch(KernelFn kernel, int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream) {
-    static std::atomic<int> allowed[kMaxDevices];
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess)
-        return err;
-    if (dev < 0 || dev >= kMaxDevices)
-        return hipErrorInvalidDevice;
-    if (allowed[dev].load(std::memory_order_acquire) == 0) {
-        err = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+// Dynamic LDS above 64 KB must be allowed once per kernel and device; each
+// kernel template instance gets its own flags.
+template <void (*Kernel)(FwdArgs)>
+hipError_t launch(int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream) {
+    if (lds > 64 * 1024) {
+        static std::atomic<int> allowed[kMaxDevices];
+        int dev = 0;
+        hipError_t err = hipGetDevice(&dev);
         if (err != hipSuccess)
             return err;
-        allowed[dev].store(1, std::memory_order_release);
+        if (dev < 0 || dev >= kMaxDevices)
+            return hipErrorInvalidDevice;
+        if (allowed[dev].load(std::memory_order_acquire) == 0) {
+            err = hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (err != hipSuccess)
+                return err;
+            allowed[dev].store(1, std::memory_order_release);
+        }
     }
-    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(kThreads), (size_t)lds, stream, args);
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)nwg), dim3(kThreads), (size_t)lds, stream, args);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_f32(int64_t nwg, const FwdArgs &args, hipStream_t stream) {
-    return launch(fa_fwd_f32_kernel<D, CAUSAL>, nwg, F32Cfg<D>::LDS, args, stream);
+    return launch<fa_fwd_f32_kernel<D, CAUSAL, SPLIT>>(nwg, F32Cfg<D>::LDS, args, stream);
 }
 
-template <typename E, int D>
+template <typename E, int D, bool SPLIT>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     if (causal)
-        return launch(fa_fwd_mfma_kernel<E, D, true>, nwg, 0, args, stream);
-    return launch(fa_fwd_mfma_kernel<E, D, false>, nwg, 0, args, stream);
+        return launch<fa_fwd_mfma_kernel<E, D, true, SPLIT>>(nwg, 0, args, stream);
+    return launch<fa_fwd_mfma_kernel<E, D, false, SPLIT>>(nwg, 0, args, stream);
+}
+
+template <bool SPLIT>
+hipError_t launch_dtype(int dtype, int D, bool causal, int64_t nwg, const FwdArgs &args,
+                        hipStream_t stream) {
+    if (dtype == 0) {
+        if (D == 64)
+            return causal ? launch_f32<64, true, SPLIT>(nwg, args, stream)
+                          : launch_f32<64, false, SPLIT>(nwg, args, stream);
+        return causal ? launch_f32<128, true, SPLIT>(nwg, args, stream)
+                      : launch_f32<128, false, SPLIT>(nwg, args, stream);
+    }
+    if (dtype == 1)
+        return D == 64 ? launch_mfma<Bf16, 64, SPLIT>(causal, nwg, args, stream)
+                       : launch_mfma<Bf16, 128, SPLIT>(causal, nwg, args, stream);
+    return D == 64 ? launch_mfma<F16, 64, SPLIT>(causal, nwg, args, stream)
+                   : launch_mfma<F16, 128, SPLIT>(causal, nwg, args, stream);
 }
 
 } // namespace
 
-hipError_t launch_fwd(int dtype, int D, bool causal, int64_t BH, const FwdArgs &args,
+hipError_t launch_fwd(int dtype, int D, bool causal, bool split, int64_t BH, const FwdArgs &args,
                       hipStream_t stream) {
-    const int64_t nwg = BH * (int64_t)args.n_qblk;
-    if (dtype == 0) {
-        if (D == 64)
-            return causal ? launch_f32<64, true>(nwg, args, stream) : launch_f32<64, false>(nwg, args, stream);
-        return causal ? launch_f32<128, true>(nwg, args, stream) : launch_f32<128, false>(nwg, args, stream);
-    }
-    if (dtype == 1)
-        return D == 64 ? launch_mfma<Bf16, 64>(causal, nwg, args, stream)
-                       : launch_mfma<Bf16, 128>(causal, nwg, args, stream);
-    return D == 64 ? launch_mfma<F16, 64>(causal, nwg, args, stream)
-                   : launch_mfma<F16, 128>(causal, nwg, args, stream);
+    // one workgroup per (slice, query block), times the key splits
+    const int64_t nwg = BH * (int64_t)args.n_qblk * (split ? args.n_splits : 1);
+    return split ? launch_dtype<true>(dtype, D, causal, nwg, args, stream)
+                 : launch_dtype<false>(dtype, D, causal, nwg, args, stream);
 }
 
 } // namespace fa

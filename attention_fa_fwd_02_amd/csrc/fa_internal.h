@@ -16,13 +16,29 @@ struct FwdArgs {
     int32_t n_qblk; // query blocks per slice: ceil(N / kQueryBlock)
     float c;        // |scale| * log2(e): scores enter exp2 through one FMA
     uint32_t qneg;  // sign-bit mask XORed onto Q words when scale < 0 (0 otherwise)
+    // key-split launches only (ignored otherwise): split s of slice bh covers
+    // keys [s * split_keys, (s + 1) * split_keys) and writes its normalised
+    // fp32 output and lse to part_o[s][bh][n][:] and part_lse[s][bh][n]
+    float *part_o;
+    float *part_lse;
+    int64_t part_rows; // rows per split in part_o / part_lse: B * H * N
+    int32_t split_keys; // a multiple of 128 (the key tile of every path)
+    int32_t n_splits;
 };
 
 // Query rows per workgroup for every path (8 waves x 32 rows).
 constexpr int kQueryBlock = 256;
 
-// Enqueue the forward pass; arguments are already validated.
-hipError_t launch_fwd(int dtype, int D, bool causal, int64_t BH, const FwdArgs &args,
+// Enqueue the forward pass; arguments are already validated.  With
+// split = true the grid covers args.n_splits key splits per query block and
+// writes part_o / part_lse instead of o / lse.
+hipError_t launch_fwd(int dtype, int D, bool causal, bool split, int64_t BH, const FwdArgs &args,
                       hipStream_t stream);
+
+// Merge n_parts partial results per row: part_o [n_parts][rows][D] fp32,
+// part_lse [n_parts][rows]; writes o [rows][D] (dtype 0 fp32, 1 bf16, 2 fp16)
+// and lse [rows].  D is a multiple of 8.
+hipError_t launch_merge(int dtype, const float *part_o, const float *part_lse, int n_parts,
+                        int64_t rows, int D, void *o, float *lse, hipStream_t stream);
 
 } // namespace fa

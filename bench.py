@@ -36,7 +36,12 @@ WORKLOADS = {
     "tiny_f32": (1, 1, 128, 64, "f32", False, (1.0, 1.0, 1.0)),
     "wide": (32, 32, 4096, 64, "bf16", False, (1.0, 1.0, 1.0)),
     "long_causal": (1, 8, 131072, 128, "bf16", True, (0.5, 0.5, 1.0)),
+    "few_heads": (1, 2, 8192, 128, "bf16", False, (1.0, 1.0, 1.0)),
+    "few_heads_causal": (1, 2, 8192, 128, "bf16", True, (1.0, 1.0, 1.0)),
 }
+# the same workloads through fa_fwd_split (key splits + lse merge; split count
+# from fa_fwd_split_choose for the device's compute units)
+SPLIT_WORKLOADS = {"few_heads_split": "few_heads", "few_heads_causal_split": "few_heads_causal"}
 
 
 def log(*a):
@@ -135,7 +140,8 @@ def bench_one(name, steps, warmup, copy_calibration=False):
 
     import attention_fa_fwd_02_amd as fa
     import fa_inputs as fi
-    B, H, N, D, dtype, causal, sigma = WORKLOADS[name]
+    split = name in SPLIT_WORKLOADS
+    B, H, N, D, dtype, causal, sigma = WORKLOADS[SPLIT_WORKLOADS.get(name, name)]
     host, (q, k, v) = device_inputs(B, H, N, D, dtype, sigma)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -148,6 +154,20 @@ def bench_one(name, steps, warmup, copy_calibration=False):
                        B, H, N, D, scale, int(causal), code, stream.cuda_stream)
         if st != fa.FA_OK:
             raise fa.FaError(st)
+
+    n_splits = 1
+    if split:
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+        n_splits = fa.fa_fwd_split_choose(B, H, N, D, int(causal), n_cus)
+        ws_bytes = fa.fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+        def step():  # noqa: F811 -- the split path replaces the single launch
+            st = fa.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, N, D, scale, int(causal), code, n_splits, ws.data_ptr(), ws_bytes,
+                                 stream.cuda_stream)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, "fa_fwd_split")
 
     if copy_calibration:
         # a plain device copy of known size, for scaling HBM byte counters
@@ -181,8 +201,8 @@ def bench_one(name, steps, warmup, copy_calibration=False):
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    log("%s: B%d H%d N%d D%d %s causal=%d  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
-        % (name, B, H, N, D, dtype, causal, ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
+    log("%s: B%d H%d N%d D%d %s causal=%d%s  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
+        % (name, B, H, N, D, dtype, causal, " splits=%d" % n_splits if split else "", ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
            100 * achieved / peak, dtype))
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
                kernel_ms=kern_ms, value=value, achieved=achieved, peak=peak, flops=flops)
@@ -195,7 +215,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS) + sorted(SPLIT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (for scaling HBM byte counters)")
@@ -215,7 +235,7 @@ def main():
     if args.all:
         # every GPU timing comes before the CPU-oracle leg, whose minutes of host
         # work would otherwise leave the GPU idle (and down-clocked) right before
-        for name in WORKLOADS:
+        for name in list(WORKLOADS) + list(SPLIT_WORKLOADS):
             if name != args.workload:
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     r = main_res

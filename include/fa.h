@@ -98,6 +98,105 @@ fa_status fa_check_args(const void *q, const void *k, const void *v, const void 
                         const float *lse, int64_t B, int64_t H, int64_t N, int64_t D,
                         float scale, int causal, int dtype, const char *arch);
 
+/*
+ * Key splits.  fa_fwd gives one workgroup per 256 query rows of a (batch,
+ * head) slice, which leaves most of the device idle when B*H*ceil(N/256) is
+ * small.  fa_fwd_split also splits the keys: each split computes the
+ * attention of every query row over its own key range, normalised within
+ * that range, plus the range's logsumexp; a second kernel merges the splits
+ * with the online-softmax merge step (KingOfEgg's FlashAttention v1 post,
+ * section 4.3: new maximum, old terms rescaled by exp(m_old - m_new)), with
+ * each split's (m, l) entering as lse_s = m_s + ln l_s:
+ *   O = sum_s exp(lse_s - lse) O_s,   lse = ln sum_s exp(lse_s).
+ * The same merge combines partial results computed anywhere else over
+ * disjoint key sets, e.g. per-device key shards in ring attention, which
+ * shares the online-softmax idea (lesson 13 "GPU 内核与 FlashAttention",
+ * hpc.payai.win, key points); fa_lse_merge exposes it on its own.
+ *
+ * Split s covers keys [s*L, min(N, (s+1)*L)) with L = 128 * ceil(T / n_splits)
+ * and T = ceil(N / 128) (whole 128-key tiles); with causal masking a row i
+ * sees only the keys j <= i of the range.  Splits past the last key, and
+ * rows that see no key of a split, are empty: lse_s = -inf, and O_s is
+ * unspecified (zero, or left as it was) and never read by the merge.
+ */
+
+#define FA_MAX_SPLITS 64
+
+/*
+ * fa_fwd_split_workspace_bytes -- bytes of device workspace fa_fwd_split
+ * needs: n_splits * B*H*N * (D + 1) * 4.  The workspace holds, from its
+ * start, part_o fp32 [n_splits][B][H][N][D] and then part_lse fp32
+ * [n_splits][B][H][N] (the per-split normalised outputs and logsumexps; the
+ * lse block starts at byte n_splits*B*H*N*D*4).  Returns 0 if an argument is
+ * < 1 or the size overflows 64 bits.  Host only, no HIP call.
+ */
+uint64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
+                                      int64_t n_splits);
+
+/*
+ * fa_fwd_split_choose -- the split count this library would pick for a
+ * device with n_cus compute units: 1 when B*H*ceil(N/256) workgroups already
+ * fill the device, else enough splits to give every compute unit one
+ * workgroup, at most one split per eight key tiles (ceil(N/128) / 8: the
+ * fp32 partials' round trip through memory must stay small next to a split's
+ * work) and at most FA_MAX_SPLITS.  Returns 0 if an argument is < 1 or causal is not
+ * 0/1.  Host only, no HIP call.
+ */
+int64_t fa_fwd_split_choose(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                            int64_t n_cus);
+
+/*
+ * fa_fwd_split -- the same result as fa_fwd (O and lse, same layout and
+ * dtype rules), computed as n_splits key splits merged on the device: two
+ * kernels enqueued on `stream`, the split kernel writing the caller's
+ * workspace and the merge kernel reading it.  Results agree with fa_fwd up to
+ * rounding (the split partials are fp32; O is rounded to `dtype` once, after
+ * the merge).
+ *
+ *   n_splits         1 .. FA_MAX_SPLITS (fa_fwd_split_choose gives a default).
+ *   workspace        device pointer, 16-byte aligned, caller-owned, at least
+ *                    fa_fwd_split_workspace_bytes(B, H, N, D, n_splits) bytes;
+ *                    overwritten (layout above; its contents after the
+ *                    call completes are the split partials).
+ *   workspace_bytes  its size in bytes.
+ *   other arguments  as for fa_fwd.
+ *
+ * Errors: the checks of fa_fwd, and FA_ERR_INVALID_ARG for n_splits < 1, a
+ * NULL or misaligned workspace, workspace_bytes below the size needed, or a
+ * workspace overlapping q, k, v, o or lse; FA_ERR_UNSUPPORTED for n_splits >
+ * FA_MAX_SPLITS or B*H*ceil(N/256)*n_splits >= 2^23 workgroups.  All checks
+ * are made before any HIP call.  The library allocates nothing.
+ */
+fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                       fa_dtype dtype, int64_t n_splits, void *workspace, uint64_t workspace_bytes,
+                       fa_stream_t stream);
+
+/*
+ * fa_lse_merge -- merge n_parts partial results per row (formula above).
+ *
+ *   part_o    device pointer, fp32 [n_parts][rows][D], 16-byte aligned; part
+ *             p row r is the normalised output over key set p.
+ *   part_lse  device pointer, fp32 [n_parts][rows], 4-byte aligned; -inf
+ *             marks an empty part (its part_o row is not read).
+ *   n_parts   1 .. 1024.  rows >= 1.
+ *   D         a power of two, 8 .. 512.
+ *   o         device pointer, [rows][D] of element type `dtype` (fp32, or
+ *             bf16 / fp16 rounded to nearest even), 16-byte aligned;
+ *             overwritten.  A row whose parts are all empty gets O = 0.
+ *   lse       device pointer, fp32 [rows], 4-byte aligned; overwritten
+ *             (-inf for a row whose parts are all empty).
+ *   stream    HIP stream the kernel is enqueued on.
+ *
+ * Errors: FA_ERR_INVALID_ARG for a NULL pointer, n_parts or rows < 1, a bad
+ * dtype, misalignment, or o / lse overlapping each other or the partials;
+ * FA_ERR_UNSUPPORTED for n_parts > 1024, D not a power of two in 8..512, or
+ * n_parts*rows*D >= 2^40; FA_ERR_HIP when a device query or the launch
+ * fails.  Checks precede any HIP call; the library allocates nothing.
+ */
+fa_status fa_lse_merge(const float *part_o, const float *part_lse, int64_t n_parts, int64_t rows,
+                       int64_t D, void *o, float *lse, fa_dtype dtype, fa_stream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

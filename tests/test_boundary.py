@@ -23,7 +23,9 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = fa.load_library()
     names = declared_functions()
-    assert set(names) == {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version",
+                          "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
+                          "fa_lse_merge"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,3 +105,105 @@ def test_python_wrapper_rejects_host_tensors():
         fa.fwd(x, x, x)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x[..., :32])
+
+
+# ------------------------------------------------------------ key splits
+
+def test_max_splits_matches_header():
+    m = re.search(r"#define FA_MAX_SPLITS (\d+)", open(HEADER).read())
+    assert fa.FA_MAX_SPLITS == int(m.group(1))
+
+
+def test_split_workspace_bytes():
+    ws = fa.fa_fwd_split_workspace_bytes
+    assert ws(2, 8, 1024, 64, 4) == 4 * 2 * 8 * 1024 * 65 * 4
+    assert ws(1, 1, 1, 128, 1) == 129 * 4
+    for bad in ((0, 1, 1, 64, 1), (1, 0, 1, 64, 1), (1, 1, 0, 64, 1), (1, 1, 1, 0, 1), (1, 1, 1, 64, 0),
+                (1, 1, 1, 64, -3)):
+        assert ws(*bad) == 0
+    assert ws(1 << 30, 1 << 30, 1 << 20, 128, 64) == 0  # overflows 64 bits
+
+
+@pytest.mark.parametrize("shape,causal,n_cus,want", [
+    ((2, 8, 1024, 64), 0, 256, 1),     # 64 workgroups, but 8 key tiles: too short to split
+    ((2, 8, 1024, 64), 1, 256, 1),
+    ((2, 8, 2048, 64), 0, 256, 2),     # 128 workgroups, 16 tiles -> 2 splits of 8 tiles
+    ((4, 16, 4096, 128), 0, 256, 1),   # 1024 workgroups already fill the device
+    ((1, 1, 128, 64), 0, 256, 1),      # one key tile: nothing to split
+    ((1, 1, 4096, 128), 0, 256, 4),    # 16 workgroups want 16 splits; 32 tiles allow 4
+    ((1, 1, 1 << 20, 128), 0, 256, 1),
+    ((1, 1, 300000, 64), 0, 100000, 64),  # capped at FA_MAX_SPLITS
+    ((1, 2, 8192, 128), 1, 256, 4),
+])
+def test_split_choose(shape, causal, n_cus, want):
+    assert fa.fa_fwd_split_choose(*shape, causal, n_cus) == want
+
+
+def test_split_choose_rejects_bad_arguments():
+    assert fa.fa_fwd_split_choose(0, 1, 64, 64, 0, 256) == 0
+    assert fa.fa_fwd_split_choose(1, 1, 64, 64, 2, 256) == 0
+    assert fa.fa_fwd_split_choose(1, 1, 64, 64, 0, 0) == 0
+
+
+WS = 0x60000000  # fake workspace address, clear of every tensor above
+WS_BYTES = 1 << 28
+
+
+def split_call(**kw):
+    a = dict(GOOD, n_splits=3, ws=WS, ws_bytes=WS_BYTES)
+    a.update(kw)
+    return fa.fa_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+                           a["scale"], a["causal"], a["dtype"], a["n_splits"], a["ws"], a["ws_bytes"], 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(B=0), dict(scale=float("nan")), dict(o=Q),           # the checks of fa_fwd
+    dict(n_splits=0), dict(n_splits=-1), dict(ws=0), dict(ws=WS + 8),
+    dict(ws_bytes=3 * 2 * 3 * 100 * 65 * 4 - 1), dict(ws=Q - 64), dict(ws=L - 256), dict(ws=O + 16),
+])
+def test_split_invalid_arguments(kw):
+    # every one is rejected on the host before any HIP call, so this is safe without a GPU
+    assert split_call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+T = 1 << 40  # address spacing for the large-grid case: no two tensors overlap
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_splits=65), dict(D=96),
+    # 2^22 workgroups pass fa_fwd's grid limit; two splits reach 2^23
+    dict(B=1 << 12, H=1 << 8, N=1024, n_splits=2, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T, ws=6 * T,
+         ws_bytes=1 << 62),
+])
+def test_split_unsupported(kw):
+    assert split_call(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_large_grid_passes_fwd_checks():
+    """The large-grid split case above is within fa_fwd's own limits."""
+    assert check(B=1 << 12, H=1 << 8, N=1024, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T) == fa.FA_OK
+
+
+PO, PL, MO, ML = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+MGOOD = dict(po=PO, pl=PL, P=3, rows=1000, D=64, o=MO, lse=ML, dtype=1)
+
+
+def merge_call(**kw):
+    a = dict(MGOOD)
+    a.update(kw)
+    return fa.fa_lse_merge(a["po"], a["pl"], a["P"], a["rows"], a["D"], a["o"], a["lse"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(po=0), dict(pl=0), dict(o=0), dict(lse=0), dict(P=0), dict(rows=0), dict(D=0), dict(dtype=3),
+    dict(po=PO + 4), dict(o=MO + 8), dict(pl=PL + 2), dict(lse=ML + 1),
+    dict(o=PO + 1024), dict(lse=PL + 64), dict(o=PL - 64), dict(lse=MO + 64),
+])
+def test_merge_invalid_arguments(kw):
+    assert merge_call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(P=1025), dict(D=4), dict(D=96), dict(D=1024), dict(rows=1 << 40),
+                                dict(P=1024, rows=1 << 24, D=512)])
+def test_merge_unsupported(kw):
+    assert merge_call(**kw) == fa.FA_ERR_UNSUPPORTED
