@@ -84,7 +84,7 @@ def device_inputs(B, H, N, D, dtype, sigma, seed=1004):
     return (q, k, v), tuple(up(x) for x in (q, k, v))
 
 
-def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=12.0):
+def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
     """The fp64 oracle, as it stands, on a bounded row sample of the same workload;
     also checks those rows of the GPU output.  Returns the JSON object."""
     import numpy as np
@@ -119,8 +119,9 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=12.0):
             worst_l = max(worst_l, float(np.abs(l_np[b, h][rows].astype(np.float64) - l_ref).max()))
         return time.perf_counter() - t0, flops, worst_o, worst_l
 
-    # calibrate on a tiny sample, then size the sample to about budget_s seconds
-    t, f, _, _ = run(8, min(4, len(heads)))
+    # calibrate on a small sample that still gives every thread several rows,
+    # then size the sample to about budget_s seconds
+    t, f, _, _ = run(min(N, 8 * threads), min(4, len(heads)))
     rate = f / max(t, 1e-6)
     per_head = 4.0 * N * D * (N / 2 if causal else N)  # flops for all rows of one head
     total_rows = max(8, int(budget_s * rate / (per_head / N)))
