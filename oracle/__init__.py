@@ -61,6 +61,14 @@ def _load():
             ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.oracle_attention_rows_general.restype = ctypes.c_int
+        lib.oracle_attention_rows_general.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int,
+        ]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -96,13 +104,15 @@ def gpu_scale(scale: float) -> float:
 
 
 def attention_rows(q_rows, k, v, rows, scale: float, causal: bool, n_threads: int = 0,
-                   key_range=None):
+                   key_range=None, causal_offset=None):
     """One [N, D] slice: outputs (O_rows [R, D], lse_rows [R]) in fp64 for the query
     positions ``rows`` (q_rows[r] is query rows[r]).  All arrays are float64.
 
     ``key_range = (lo, hi)`` restricts the keys to lo <= j < hi (the partial
     result of one key split); a row with no visible key gets lse = -inf and
-    O = 0."""
+    O = 0.  ``causal_offset`` (n_keys - n_queries) switches to a slice whose
+    query count differs from its key count: causal query i then sees keys
+    j <= i + causal_offset (bottom-right alignment); None means square."""
     lib = _load()
     q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -115,10 +125,16 @@ def attention_rows(q_rows, k, v, rows, scale: float, causal: bool, n_threads: in
     o = np.empty((rows.shape[0], d), dtype=np.float64)
     lse = np.empty((rows.shape[0],), dtype=np.float64)
     lo, hi = (0, n_keys) if key_range is None else (int(key_range[0]), int(key_range[1]))
-    rc = lib.oracle_attention_rows_range(
-        q_rows.ctypes.data, k.ctypes.data, v.ctypes.data, n_keys, d,
-        rows.ctypes.data, rows.shape[0], lo, hi, float(scale), int(bool(causal)),
-        o.ctypes.data, lse.ctypes.data, int(n_threads))
+    if causal_offset is None:
+        rc = lib.oracle_attention_rows_range(
+            q_rows.ctypes.data, k.ctypes.data, v.ctypes.data, n_keys, d,
+            rows.ctypes.data, rows.shape[0], lo, hi, float(scale), int(bool(causal)),
+            o.ctypes.data, lse.ctypes.data, int(n_threads))
+    else:
+        rc = lib.oracle_attention_rows_general(
+            q_rows.ctypes.data, k.ctypes.data, v.ctypes.data, n_keys, d,
+            rows.ctypes.data, rows.shape[0], lo, hi, float(scale), int(bool(causal)),
+            int(causal_offset), o.ctypes.data, lse.ctypes.data, int(n_threads))
     if rc != 0:
         raise ValueError("oracle_attention_rows failed with code %d" % rc)
     return o, lse
@@ -143,6 +159,38 @@ def attention(q, k, v, scale: float, causal: bool, n_threads: int = 0, key_range
         o[s], lse[s] = attention_rows(qf[s], kf[s], vf[s], rows, scale, causal, n_threads,
                                       key_range)
     return o.reshape(*lead, n, d), lse.reshape(*lead, n)
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, n_threads: int = 0,
+                     seqs=None, rows_of=None):
+    """Packed variable-length sequences, head-major: q [H, total_q, D], k and v
+    [H, total_k, D]; sequence b holds query rows cu_q[b]..cu_q[b+1]-1 and key rows
+    cu_k[b]..cu_k[b+1]-1 of every head.  Each (sequence, head) is one slice with
+    n_q = cu_q[b+1] - cu_q[b] queries and n_k keys, causal aligned bottom-right
+    (query i sees keys j <= i + n_k - n_q); a row that sees no key gets lse = -inf
+    and O = 0, as does every row of a sequence with no keys.
+
+    ``seqs`` limits the work to some sequences and ``rows_of(b)`` to some rows of
+    each (positions within the sequence).  Returns a list of
+    (b, rows, O [H, R, D], lse [H, R]) in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    H, _, d = q.shape
+    out = []
+    for b in (range(len(cu_q) - 1) if seqs is None else seqs):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        rows = np.arange(q1 - q0, dtype=np.int64) if rows_of is None else np.asarray(rows_of(b), np.int64)
+        o = np.zeros((H, rows.size, d))
+        lse = np.full((H, rows.size), -np.inf)
+        if k1 > k0 and rows.size:
+            for h in range(H):
+                o[h], lse[h] = attention_rows(q[h, q0 + rows], k[h, k0:k1], v[h, k0:k1], rows, scale,
+                                              causal, n_threads, causal_offset=(k1 - k0) - (q1 - q0))
+        out.append((b, rows, o, lse))
+    return out
 
 
 def lse_merge(part_o, part_lse):

@@ -23,6 +23,12 @@
  * gives the partial result of one key split.  An empty J(i) gives the empty
  * sum: l_i = 0, m_i = -inf, lse_i = ln 0 = -inf, O_i = 0.
  *
+ * With n_q queries and n_k keys of different counts (packed variable-length
+ * sequences, cross attention), causal masking is aligned at the bottom
+ * right: query i sees keys j <= i + (n_k - n_q), so the last query sees
+ * every key.  For n_q = n_k this is the top-left mask above; the caller
+ * passes the offset n_k - n_q.
+ *
  * Sources (pages on the FlashAttention forward pass):
  *   - the three-line definition S = QK^T/sqrt(d_k), P = softmax(S), O = PV
  *     and the statement that each row of P is a probability distribution:
@@ -65,20 +71,21 @@ int oracle_default_threads(void)
  * One (batch, head) slice, keys restricted to [key_lo, key_hi).
  *   q_rows    [n_rows, d]   the query rows to evaluate (row r is query index row_index[r])
  *   k, v      [n_keys, d]   all keys and values of the slice
- *   row_index [n_rows]      query position of each row (0 <= row_index[r] < n_keys)
+ *   row_index [n_rows]      query position of each row (>= 0)
  *   key_lo, key_hi          key range, 0 <= key_lo <= key_hi <= n_keys
  *   scale                   multiplies every dot product
- *   causal                  0: keys of the range; 1: those up to row_index[r]
+ *   causal                  0: keys of the range; 1: those j <= row_index[r] + causal_offset
+ *   causal_offset           n_keys - n_queries of the slice (0 for square attention)
  *   o_rows    [n_rows, d]   output rows (fp64)
  *   lse_rows  [n_rows]      natural-log logsumexp of the scaled scores (fp64)
  *   n_threads               OpenMP threads (<= 0: the runtime default)
  * Returns 0 on success, 1 on an invalid argument, 2 if memory ran out.
  */
-int oracle_attention_rows_range(const double *q_rows, const double *k, const double *v,
-                                int64_t n_keys, int64_t d, const int64_t *row_index,
-                                int64_t n_rows, int64_t key_lo, int64_t key_hi,
-                                double scale, int causal, double *o_rows, double *lse_rows,
-                                int n_threads)
+int oracle_attention_rows_general(const double *q_rows, const double *k, const double *v,
+                                  int64_t n_keys, int64_t d, const int64_t *row_index,
+                                  int64_t n_rows, int64_t key_lo, int64_t key_hi,
+                                  double scale, int causal, int64_t causal_offset,
+                                  double *o_rows, double *lse_rows, int n_threads)
 {
     if (!q_rows || !k || !v || !row_index || !o_rows || !lse_rows)
         return 1;
@@ -87,7 +94,7 @@ int oracle_attention_rows_range(const double *q_rows, const double *k, const dou
     if (key_lo < 0 || key_hi < key_lo || key_hi > n_keys)
         return 1;
     for (int64_t r = 0; r < n_rows; r++)
-        if (row_index[r] < 0 || row_index[r] >= n_keys)
+        if (row_index[r] < 0)
             return 1;
     if (!isfinite(scale))
         return 1;
@@ -111,7 +118,8 @@ int oracle_attention_rows_range(const double *q_rows, const double *k, const dou
             const double *qi = q_rows + r * d;
             double *oi = o_rows + r * d;
             /* key set J(i) = [key_lo, j_end); S[j - key_lo] holds key j */
-            const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;
+            const int64_t j_vis = i + causal_offset + 1; /* causal: keys below j_vis */
+            const int64_t j_end = causal ? (j_vis < key_hi ? j_vis : key_hi) : key_hi;
 
             /* explicit score row: dot product first, then the scale */
             for (int64_t j = key_lo; j < j_end; j++) {
@@ -150,7 +158,23 @@ int oracle_attention_rows_range(const double *q_rows, const double *k, const dou
     return failed ? 2 : 0;
 }
 
-/* The whole key range: softmax(scale * q k^T) v over J(i). */
+/* Square attention (query positions are key positions), keys in [key_lo, key_hi). */
+int oracle_attention_rows_range(const double *q_rows, const double *k, const double *v,
+                                int64_t n_keys, int64_t d, const int64_t *row_index,
+                                int64_t n_rows, int64_t key_lo, int64_t key_hi,
+                                double scale, int causal, double *o_rows, double *lse_rows,
+                                int n_threads)
+{
+    if (!row_index)
+        return 1;
+    for (int64_t r = 0; r < n_rows; r++)
+        if (row_index[r] >= n_keys)
+            return 1;
+    return oracle_attention_rows_general(q_rows, k, v, n_keys, d, row_index, n_rows, key_lo,
+                                         key_hi, scale, causal, 0, o_rows, lse_rows, n_threads);
+}
+
+/* Square attention over the whole key range: softmax(scale * q k^T) v over J(i). */
 int oracle_attention_rows(const double *q_rows, const double *k, const double *v,
                           int64_t n_keys, int64_t d, const int64_t *row_index,
                           int64_t n_rows, double scale, int causal,

@@ -46,8 +46,8 @@ MUTATIONS = {
     "value_row_reversed": [("const double *vj = v + j * d;",
                             "const double *vj = v + (j_end - 1 - j + key_lo) * d;")],
     "value_column_shifted": [("oi[c] += p * vj[c];", "oi[c] += p * vj[(c + 1) % d];")],
-    "causal_sees_next_key": [("const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;",
-                              "const int64_t j_end = causal ? (i + 2 < key_hi ? i + 2 : key_hi) : key_hi;")],
+    "causal_sees_next_key": [("const int64_t j_end = causal ? (j_vis < key_hi ? j_vis : key_hi) : key_hi;",
+                              "const int64_t j_end = causal ? (j_vis + 1 < key_hi ? j_vis + 1 : key_hi) : key_hi;")],
     "lse_in_log2": [("lse_rows[r] = m + log(l);", "lse_rows[r] = m + log2(l);")],
     "lse_without_max": [("lse_rows[r] = m + log(l);", "lse_rows[r] = log(l);")],
 }

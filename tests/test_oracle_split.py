@@ -221,10 +221,10 @@ PARTIAL_MUTATIONS = {
                                        "const double *vj = v + (j - key_lo) * d;")],
     "key_index_relative_to_range": [("const double *kj = k + j * d;",
                                      "const double *kj = k + (j - key_lo) * d;")],
-    "causal_range_drops_diagonal": [("const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;",
-                                     "const int64_t j_end = causal ? (i < key_hi ? i : key_hi) : key_hi;")],
-    "range_ignores_upper_end": [("const int64_t j_end = causal ? (i + 1 < key_hi ? i + 1 : key_hi) : key_hi;",
-                                 "const int64_t j_end = causal ? i + 1 : n_keys;")],
+    "causal_range_drops_diagonal": [("const int64_t j_end = causal ? (j_vis < key_hi ? j_vis : key_hi) : key_hi;",
+                                     "const int64_t j_end = causal ? (j_vis - 1 < key_hi ? j_vis - 1 : key_hi) : key_hi;")],
+    "range_ignores_upper_end": [("const int64_t j_end = causal ? (j_vis < key_hi ? j_vis : key_hi) : key_hi;",
+                                 "const int64_t j_end = causal ? j_vis : n_keys;")],
 }
 
 
