@@ -7,10 +7,10 @@ device is not gfx950 the calls raise.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
 ``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
-``fa_status_string``, ``fa_abi_version``.  ``fwd``, ``fwd_split`` and
-``lse_merge`` are convenience wrappers that allocate outputs (and the split
-workspace) with torch (device memory and the current stream are all torch
-provides).
+``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_status_string``,
+``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen`` and ``lse_merge``
+are convenience wrappers that allocate outputs (and the split workspace) with
+torch (device memory and the current stream are all torch provides).
 """
 from __future__ import annotations
 
@@ -21,8 +21,8 @@ import os
 __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_MAX_SPLITS", "FaError", "lib_path",
            "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
-           "fa_fwd_split_choose", "fa_lse_merge", "fa_status_string", "fa_abi_version",
-           "fwd", "fwd_split", "lse_merge"]
+           "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
+           "fa_status_string", "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -67,6 +67,12 @@ def load_library():
         lib.fa_fwd_split_choose.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64]
         lib.fa_lse_merge.restype = ctypes.c_int
         lib.fa_lse_merge.argtypes = [vp, vp, i64, i64, i64, vp, vp, ctypes.c_int, vp]
+        lib.fa_fwd_varlen.restype = ctypes.c_int
+        lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                      ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        lib.fa_check_varlen_args.restype = ctypes.c_int
+        lib.fa_check_varlen_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_char_p]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -118,6 +124,23 @@ def fa_lse_merge(part_o: int, part_lse: int, n_parts: int, rows: int, D: int, o:
                  dtype: int, stream: int) -> int:
     """Raw C call with integer device addresses; returns the fa_status code."""
     return int(load_library().fa_lse_merge(part_o, part_lse, n_parts, rows, D, o, lse, dtype, stream))
+
+
+def fa_fwd_varlen(q: int, k: int, v: int, o: int, lse: int, cu_q: int, cu_k: int, n_seqs: int,
+                  H: int, total_q: int, total_k: int, max_seqlen_q: int, D: int, scale: float,
+                  causal: int, dtype: int, stream: int) -> int:
+    """Raw C call with integer device addresses; returns the fa_status code."""
+    return int(load_library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, n_seqs, H, total_q, total_k,
+                                            max_seqlen_q, D, scale, causal, dtype, stream))
+
+
+def fa_check_varlen_args(q: int, k: int, v: int, o: int, lse: int, cu_q: int, cu_k: int, n_seqs: int,
+                         H: int, total_q: int, total_k: int, max_seqlen_q: int, D: int, scale: float,
+                         causal: int, dtype: int, arch: str | None = None) -> int:
+    """Host-only argument check of fa_fwd_varlen (no HIP call); returns the fa_status code."""
+    a = arch.encode() if arch is not None else None
+    return int(load_library().fa_check_varlen_args(q, k, v, o, lse, cu_q, cu_k, n_seqs, H, total_q,
+                                                   total_k, max_seqlen_q, D, scale, causal, dtype, a))
 
 
 def _dtype_code(t) -> int:
@@ -211,6 +234,48 @@ def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, n_split
     if st != FA_OK:
         raise FaError(st, "fa_fwd_split")
     return out, lse, workspace
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: float | None = None,
+               causal: bool = False, out=None, lse=None, stream=None):
+    """Packed variable-length attention (fa_fwd_varlen).
+
+    q [H, total_q, D], k and v [H, total_k, D] CUDA tensors (head-major packing);
+    cu_seqlens_q / cu_seqlens_k int32 CUDA tensors [n_seqs + 1]; causal masks are
+    aligned at the bottom right.  Returns (O [H, total_q, D], lse [H, total_q]).
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [H, total_q, D] and k, v [H, total_k, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda:
+            raise ValueError("%s is not a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise TypeError("%s must be a 1-D int32 tensor" % name)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold n_seqs + 1 >= 2 entries")
+    H, total_q, D = q.shape
+    total_k = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, H,
+                           total_q, total_k, int(max_seqlen_q), D, float(scale), int(bool(causal)),
+                           _dtype_code(q.dtype), handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_varlen")
+    return out, lse
 
 
 def lse_merge(part_o, part_lse, out_dtype=None, out=None, lse=None, stream=None):

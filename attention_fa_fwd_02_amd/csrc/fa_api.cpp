@@ -150,7 +150,7 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     if ((st = check_device()) != FA_OK)
         return st;
     const fa::FwdArgs args = make_args(q, k, v, o, lse, N, scale, dtype);
-    const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, false, B * H, args,
+    const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kDense, B * H, args,
                                           reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -218,10 +218,77 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
     args.split_keys = (int32_t)split_keys(N, n_splits);
     args.n_splits = (int32_t)n_splits;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, true, BH, args, hs);
+    hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kSplit, BH * n_splits, args, hs);
     if (err == hipSuccess)
         err = fa::launch_merge((int)dtype, args.part_o, args.part_lse, (int)n_splits, rows, (int)D, o,
                                lse, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_check_varlen_args(const void *q, const void *k, const void *v, const void *o,
+                               const float *lse, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, int64_t n_seqs, int64_t H, int64_t total_q,
+                               int64_t total_k, int64_t max_seqlen_q, int64_t D, float scale, int causal,
+                               int dtype, const char *arch) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k)
+        return FA_ERR_INVALID_ARG;
+    if (n_seqs < 1 || H < 1 || total_q < 1 || total_k < 1 || D < 1)
+        return FA_ERR_INVALID_ARG;
+    if (max_seqlen_q < 1 || max_seqlen_q > total_q)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || (causal != 0 && causal != 1))
+        return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
+        return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128)
+        return FA_ERR_UNSUPPORTED;
+    if (total_q >= (int64_t(1) << 30) || total_k >= (int64_t(1) << 30) || n_seqs >= (int64_t(1) << 30) ||
+        H >= (int64_t(1) << 20))
+        return FA_ERR_UNSUPPORTED;
+    if (H * total_q >= (int64_t(1) << 36) || H * total_k >= (int64_t(1) << 36))
+        return FA_ERR_UNSUPPORTED;
+    const int64_t n_qblk = (max_seqlen_q + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    if (n_seqs * H * n_qblk >= (int64_t(1) << 23))
+        return FA_ERR_UNSUPPORTED;
+    const uint64_t qbytes = (uint64_t)(H * total_q * D) * elem_size(dtype);
+    const uint64_t kbytes = (uint64_t)(H * total_k * D) * elem_size(dtype);
+    const uint64_t lbytes = (uint64_t)(H * total_q) * 4u;
+    const uint64_t cbytes = (uint64_t)(n_seqs + 1) * 4u;
+    const void *ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+    const uint64_t in_bytes[5] = {qbytes, kbytes, kbytes, cbytes, cbytes};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(o, qbytes, ins[i], in_bytes[i]) || overlaps(lse, lbytes, ins[i], in_bytes[i]))
+            return FA_ERR_INVALID_ARG;
+    if (overlaps(o, qbytes, lse, lbytes))
+        return FA_ERR_INVALID_ARG;
+    if (arch && std::strncmp(arch, "gfx950", 6) != 0)
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t n_seqs,
+                        int64_t H, int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t D,
+                        float scale, int causal, fa_dtype dtype, fa_stream_t stream) {
+    fa_status st = fa_check_varlen_args(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, H, total_q,
+                                        total_k, max_seqlen_q, D, scale, causal, (int)dtype, nullptr);
+    if (st != FA_OK)
+        return st;
+    if ((st = check_device()) != FA_OK)
+        return st;
+    fa::FwdArgs args = make_args(q, k, v, o, lse, 0, scale, dtype);
+    args.n_qblk = (int32_t)((max_seqlen_q + fa::kQueryBlock - 1) / fa::kQueryBlock);
+    args.cu_q = cu_seqlens_q;
+    args.cu_k = cu_seqlens_k;
+    args.n_heads = (int32_t)H;
+    args.total_q = (int32_t)total_q;
+    args.total_k = (int32_t)total_k;
+    const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kVarlen, n_seqs * H, args,
+                                          reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -171,6 +171,51 @@ __device__ __forceinline__ Work map_workgroup(int wg, int nwg, int n_qblk, bool 
     return w;
 }
 
+// Packed sequences differ in length, so contiguous ranges of grid rows per
+// XCD (as above) can leave one XCD with several times the work of another.
+// Here grid row r goes to XCD r % 8 (each XCD gets every eighth head of every
+// sequence: balanced, and a row's query blocks still share one L2), and each
+// XCD hands out its rows' query blocks highest block index first: only long
+// sequences have high blocks, so long work starts early, and causal blocks
+// come longest first.
+__device__ __forceinline__ Work map_workgroup_strided(int wg, int nwg, int n_qblk, bool causal) {
+    const int rows = nwg / n_qblk;
+    if ((rows & 7) == 0) {
+        const int per_x = rows >> 3; // rows per XCD
+        const int x = wg & 7, j = wg >> 3;
+        const int lvl = j / per_x; // 0 .. n_qblk-1, highest query block first
+        Work w;
+        w.bh = (j - lvl * per_x) * 8 + x;
+        w.qb = n_qblk - 1 - lvl;
+        return w;
+    }
+    Work w;
+    const int lvl = wg / rows;
+    w.bh = wg - lvl * rows;
+    w.qb = n_qblk - 1 - lvl;
+    return w;
+}
+
+// One packed variable-length sequence of a (sequence, head) grid row: the
+// sequence bounds are clamped into the packed tensors, so any cu_seqlens
+// contents keep every access in bounds.
+struct SeqSlice {
+    int nq, nk;
+    int64_t q_off, k_off, lse_off;
+};
+__device__ __forceinline__ SeqSlice seq_slice(const FwdArgs &a, int row, int D) {
+    const int b = row / a.n_heads, h = row - b * a.n_heads;
+    const int cq0 = min(max(a.cu_q[b], 0), a.total_q), cq1 = min(max(a.cu_q[b + 1], cq0), a.total_q);
+    const int ck0 = min(max(a.cu_k[b], 0), a.total_k), ck1 = min(max(a.cu_k[b + 1], ck0), a.total_k);
+    SeqSlice s;
+    s.nq = cq1 - cq0;
+    s.nk = ck1 - ck0;
+    s.q_off = ((int64_t)h * a.total_q + cq0) * D;
+    s.k_off = ((int64_t)h * a.total_k + ck0) * D;
+    s.lse_off = (int64_t)h * a.total_q + cq0;
+    return s;
+}
+
 // ----------------------------------------------------------------------------
 // 16-bit element types
 // ----------------------------------------------------------------------------
@@ -222,8 +267,9 @@ struct MfmaCfg {
     static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
 };
 
-template <typename E, int D, bool CAUSAL, bool SPLIT>
+template <typename E, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
+    constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
     using Cfg = MfmaCfg<D>;
     constexpr int BC = Cfg::BC;
     constexpr int KB = BC / 32; // 32-key MFMA blocks per tile
@@ -245,37 +291,66 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31;
     const int g = lane >> 5;
-    const int N = a.N;
 
-    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    const Work wk = VARLEN ? map_workgroup_strided(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL)
+                           : map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
     // a key-split grid has n_splits rows per slice: (slice, split) = divmod(row)
     const int bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
     const int split = SPLIT ? wk.bh - bh * a.n_splits : 0;
-    const int64_t slice = (int64_t)bh * N * D;
-    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + slice;
-    const uint16_t *__restrict__ K = (const uint16_t *)a.k + slice;
-    const uint16_t *__restrict__ V = (const uint16_t *)a.v + slice;
-    uint16_t *__restrict__ O = (uint16_t *)a.o + slice;
-    float *__restrict__ LSE = a.lse + (int64_t)bh * N;
+    // the slice: Nq query rows and Nk keys; causal query i sees keys
+    // j <= i + coff (bottom-right alignment; coff = 0 for square slices)
+    const SeqSlice sq = VARLEN ? seq_slice(a, wk.bh, D) : SeqSlice{};
+    const int Nq = VARLEN ? sq.nq : a.N;
+    const int Nk = VARLEN ? sq.nk : a.N;
+    const int coff = VARLEN ? sq.nk - sq.nq : 0;
+    // element offsets of the slice's first query / key row and lse entry
+    const int64_t q_off = VARLEN ? sq.q_off : (int64_t)bh * a.N * D;
+    const int64_t k_off = VARLEN ? sq.k_off : (int64_t)bh * a.N * D;
+    const int64_t lse_off = VARLEN ? sq.lse_off : (int64_t)bh * a.N;
+    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + q_off;
+    const uint16_t *__restrict__ K = (const uint16_t *)a.k + k_off;
+    const uint16_t *__restrict__ V = (const uint16_t *)a.v + k_off;
+    uint16_t *__restrict__ O = (uint16_t *)a.o + q_off;
+    float *__restrict__ LSE = a.lse + lse_off;
 
     const int q0 = wk.qb * kQueryBlock;
     const int q0w = q0 + 32 * wave; // first query row of this wave
     const int qi = q0w + r;         // this lane's query row
+    if (VARLEN && q0 >= Nq) // the grid covers the longest sequence
+        return;
     // keys [k_begin, kv_end): the split's range (whole key tiles) cut at the
     // last key any row of the block sees
     const int k_begin = SPLIT ? split * a.split_keys : 0;
-    const int kv_vis = CAUSAL ? min(N, q0 + kQueryBlock) : N;
+    const int kv_vis = CAUSAL ? min(Nk, q0 + kQueryBlock + coff) : Nk;
     const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
-    const int n_tiles = SPLIT ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
-                              : (kv_end + BC - 1) / BC;
+    const int n_tiles = (SPLIT || VARLEN) ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
+                                          : (kv_end + BC - 1) / BC;
     if constexpr (SPLIT) {
-        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * N;
+        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * a.N;
         if (n_tiles == 0) { // no key of this split is visible to the block
-            if (tid < kQueryBlock && q0 + tid < N)
+            if (tid < kQueryBlock && q0 + tid < Nq)
                 PLSE[q0 + tid] = -INFINITY;
             return;
         }
     }
+    if constexpr (VARLEN) {
+        if (n_tiles == 0) { // no key is visible to any row of the block: O = 0, lse = -inf
+            if (tid < kQueryBlock && q0 + tid < Nq) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < D / 8; ++c)
+                    *(u32x4 *)(O + (int64_t)(q0 + tid) * D + 8 * c) = z;
+                LSE[q0 + tid] = -INFINITY;
+            }
+            return;
+        }
+    }
+
+    // causal packed sequences: tiles t < n_act_w hold a key this wave's rows can
+    // see (stated through the tile index: the compiler then keeps the same
+    // register allocation as for square slices)
+    const int last_w = q0w + 31 + coff - k_begin;
+    const int n_act_w = last_w < 0 ? 0 : last_w / BC + 1;
 
     // --- tile loader: direct global -> LDS buffer loads -----------------------
     // Load j of wave w fills 1 KB block b = w + 8j of the stage: lane l writes
@@ -334,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     u32x4 qf[DC];
 #pragma unroll
     for (int cc = 0; cc < DC; ++cc) {
-        qf[cc] = qi < N ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
+        qf[cc] = qi < Nq ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
         qf[cc] ^= a.qneg;
     }
 
@@ -351,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // t+1 visible
     auto tile = [&](int t, const lds_char *cur, lds_char *next) {
         const int k0 = k_begin + t * BC;
-        const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
+        const bool active = (q0w < Nq) && (!CAUSAL || (VARLEN ? t < n_act_w : k0 <= q0w + 31));
         if (active) {
             const lds_char *ks = cur + k_lane;
             const lds_char *vs = cur + Cfg::KST + v_lane;
@@ -379,16 +454,28 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
             // the next tile's loads go out after the score phase, so their LDS
             // writes do not land among its K reads
             issue_tile(t + 1, next);
-            // masking: keys beyond N, and keys after the query when causal
-            if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
+            // masking: keys beyond Nk, and keys after the query when causal
+            if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff)) {
+                if constexpr (VARLEN) {
+                    // entry (kb, i) is key k0 + g + e with e = 32 kb + 2 i; one
+                    // per-lane bound against the compile-time e keeps the mask
+                    // free of per-entry registers
+                    const int lim = CAUSAL ? min(Nk, qi + coff + 1) - k0 - g : Nk - k0 - g;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + 32 * kb + 2 * i + g;
-                        const bool vis = key < N && (!CAUSAL || key <= qi);
-                        s[kb][i] = vis ? s[kb][i] : -INFINITY;
-                    }
+                        for (int i = 0; i < 16; ++i)
+                            s[kb][i] = (32 * kb + 2 * i < lim) ? s[kb][i] : -INFINITY;
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = k0 + 32 * kb + 2 * i + g;
+                            const bool vis = key < Nk && (!CAUSAL || key <= qi + coff);
+                            s[kb][i] = vis ? s[kb][i] : -INFINITY;
+                        }
+                }
             }
             // online softmax against the current reference m_ref:
             // P~ = exp2(s*c - m_ref), summed in fp32, then rounded for the PV MFMA
@@ -480,11 +567,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
         static_assert(4 * 32 * OP4 <= Cfg::STAGE, "four waves' fp32 O rows fit in one stage");
-        float *__restrict__ PO = a.part_o + (split * a.part_rows + (int64_t)bh * N) * D;
-        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * N;
+        float *__restrict__ PO = a.part_o + (split * a.part_rows + (int64_t)bh * a.N) * D;
+        float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * a.N;
         tile_barrier();
         lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4;
-        if (q0w < N) {
+        if (q0w < Nq) {
 #pragma unroll
             for (int b = 0; b < OB; ++b)
 #pragma unroll
@@ -493,11 +580,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                                      o[b][4 * a4 + 3] * inv};
                     *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
                 }
-            if (g == 0 && qi < N)
+            if (g == 0 && qi < Nq)
                 PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
         }
         __syncthreads();
-        if (q0w < N) {
+        if (q0w < Nq) {
             constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
 #pragma unroll
             for (int j = 0; j < kChunks / 64; ++j) {
@@ -505,17 +592,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                 const int row = ch / (D / 4), col = ch % (D / 4);
                 const int q = q0w + row;
                 const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
-                if (q < N)
+                if (q < Nq)
                     *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
             }
         }
         return;
     }
-    const float inv = 1.0f / l_tot;
+    // (packed sequences: a row that sees no key has l = 0 and gets O = 0, lse = -inf)
+    const float inv = (VARLEN && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
     static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
     tile_barrier();
     lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
-    if (q0w < N) {
+    if (q0w < Nq) {
 #pragma unroll
         for (int b = 0; b < OB; ++b)
 #pragma unroll
@@ -524,11 +612,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
                                  E::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
                 *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
             }
-        if (g == 0 && qi < N)
+        if (g == 0 && qi < Nq)
             LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
     __syncthreads();
-    if (q0w < N) {
+    if (q0w < Nq) {
         constexpr int kChunks = 32 * KCH; // 16-byte chunks in the wave's 32 rows
 #pragma unroll
         for (int j = 0; j < kChunks / 64; ++j) {
@@ -536,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
             const int row = ch / KCH, col = ch % KCH;
             const int q = q0w + row;
             const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
-            if (q < N)
+            if (q < Nq)
                 *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
         }
     }
@@ -554,8 +642,9 @@ struct F32Cfg {
     static constexpr int LDS = 2 * STAGE;
 };
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
+    constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
     using Cfg = F32Cfg<D>;
     constexpr int BC = Cfg::BC;
     constexpr int KP = Cfg::KP;
@@ -571,32 +660,59 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     const int wave = tid >> 6;
     const int r = lane & 31;
     const int g = lane >> 5;
-    const int N = a.N;
 
-    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
-    const int bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
-    const int split = SPLIT ? wk.bh - bh * a.n_splits : 0;
-    const int64_t slice = (int64_t)bh * N * D;
-    const float *__restrict__ Q = (const float *)a.q + slice;
-    const float *__restrict__ K = (const float *)a.k + slice;
-    const float *__restrict__ V = (const float *)a.v + slice;
+    const Work wk = VARLEN ? map_workgroup_strided(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL)
+                           : map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    // slice geometry as in the MFMA kernel: Nq rows, Nk keys, causal offset coff
+    int bh = wk.bh, split = 0, Nq = a.N, Nk = a.N, coff = 0;
+    int64_t q_off, k_off, lse_off;
+    if constexpr (SPLIT) {
+        bh = wk.bh / a.n_splits;
+        split = wk.bh - bh * a.n_splits;
+    }
+    if constexpr (VARLEN) {
+        const int b = wk.bh / a.n_heads, h = wk.bh - b * a.n_heads;
+        const int cq0 = min(max(a.cu_q[b], 0), a.total_q), cq1 = min(max(a.cu_q[b + 1], cq0), a.total_q);
+        const int ck0 = min(max(a.cu_k[b], 0), a.total_k), ck1 = min(max(a.cu_k[b + 1], ck0), a.total_k);
+        Nq = cq1 - cq0;
+        Nk = ck1 - ck0;
+        coff = Nk - Nq;
+        q_off = ((int64_t)h * a.total_q + cq0) * D;
+        k_off = ((int64_t)h * a.total_k + ck0) * D;
+        lse_off = (int64_t)h * a.total_q + cq0;
+    } else {
+        q_off = k_off = (int64_t)bh * a.N * D;
+        lse_off = (int64_t)bh * a.N;
+    }
+    const float *__restrict__ Q = (const float *)a.q + q_off;
+    const float *__restrict__ K = (const float *)a.k + k_off;
+    const float *__restrict__ V = (const float *)a.v + k_off;
     // a key split writes its normalised fp32 partial in place of O and lse
-    float *__restrict__ O = SPLIT ? a.part_o + (split * a.part_rows + (int64_t)bh * N) * D
-                                  : (float *)a.o + slice;
-    float *__restrict__ LSE = SPLIT ? a.part_lse + split * a.part_rows + (int64_t)bh * N
-                                    : a.lse + (int64_t)bh * N;
+    float *__restrict__ O = SPLIT ? a.part_o + (split * a.part_rows + (int64_t)bh * a.N) * D
+                                  : (float *)a.o + q_off;
+    float *__restrict__ LSE = SPLIT ? a.part_lse + split * a.part_rows + (int64_t)bh * a.N
+                                    : a.lse + lse_off;
 
     const int q0 = wk.qb * kQueryBlock;
     const int q0w = q0 + 32 * wave;
     const int qi = q0w + r;
+    if (VARLEN && q0 >= Nq) // the grid covers the longest sequence
+        return;
     const int k_begin = SPLIT ? split * a.split_keys : 0;
-    const int kv_vis = CAUSAL ? min(N, q0 + kQueryBlock) : N;
+    const int kv_vis = CAUSAL ? min(Nk, q0 + kQueryBlock + coff) : Nk;
     const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
-    const int n_tiles = SPLIT ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
-                              : (kv_end + BC - 1) / BC;
-    if (SPLIT && n_tiles == 0) { // no key of this split is visible to the block
-        if (tid < kQueryBlock && q0 + tid < N)
+    const int n_tiles = (SPLIT || VARLEN) ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
+                                          : (kv_end + BC - 1) / BC;
+    if ((SPLIT || VARLEN) && n_tiles == 0) { // no key is visible to any row of the block
+        if (tid < kQueryBlock && q0 + tid < Nq) {
+            if (VARLEN) { // O = 0 (a split leaves an empty partial's O unwritten)
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < D / 4; ++c)
+                    *(f32x4 *)(O + (int64_t)(q0 + tid) * D + 4 * c) = z;
+            }
             LSE[q0 + tid] = -INFINITY;
+        }
         return;
     }
 
@@ -614,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int key = k0 + ckey[i];
-            const bool ok = key < N;
+            const bool ok = key < Nk;
             kr[i] = ok ? *(const f32x4 *)(K + (int64_t)key * D + ccol[i]) : zero4;
             vr[i] = ok ? *(const f32x4 *)(V + (int64_t)key * D + ccol[i]) : zero4;
         }
@@ -637,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         const float sgn = a.qneg ? -1.f : 1.f;
 #pragma unroll
         for (int j = 0; j < H2; j += 4) {
-            const f32x4 x = qi < N ? *(const f32x4 *)(Q + (int64_t)qi * D + H2 * g + j) : zero4;
+            const f32x4 x = qi < Nq ? *(const f32x4 *)(Q + (int64_t)qi * D + H2 * g + j) : zero4;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 qf[j + e] = sgn * x[e];
@@ -660,7 +776,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         if (t + 1 < n_tiles)
             load_tile(t + 1);
         const int k0 = k_begin + t * BC;
-        const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
+        const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + 31 + coff);
         if (active) {
             const float *ks = (const float *)(smem + stage * Cfg::STAGE);
             const float *vs = (const float *)(smem + stage * Cfg::STAGE + Cfg::KSTAGE);
@@ -670,12 +786,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
             for (int j = 0; j < H2; ++j)
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[j], qf[j], s, 0, 0, 0);
-            const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w);
+            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff);
             if (need_mask) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = k0 + 16 * g + i;
-                    const bool vis = key < N && (!CAUSAL || key <= qi);
+                    const bool vis = key < Nk && (!CAUSAL || key <= qi + coff);
                     s[i] = vis ? s[i] : -INFINITY;
                 }
             }
@@ -713,11 +829,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         __syncthreads();
     }
 
-    if (q0w < N) {
+    if (q0w < Nq) {
         const float l_tot = pair_sum(l_run);
-        // a split row that sees no key: l = 0, m = -inf -> O = 0, lse = -inf
-        const float inv = (SPLIT && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
-        if (qi < N) {
+        // a row that sees no key (split or packed sequence): l = 0, m = -inf -> O = 0, lse = -inf
+        const float inv = ((SPLIT || VARLEN) && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
+        if (qi < Nq) {
             float *orow = O + (int64_t)qi * D + 16 * g;
 #pragma unroll
             for (int b = 0; b < OB; ++b)
@@ -759,44 +875,47 @@ hipError_t launch(int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch_f32(int64_t nwg, const FwdArgs &args, hipStream_t stream) {
-    return launch<fa_fwd_f32_kernel<D, CAUSAL, SPLIT>>(nwg, F32Cfg<D>::LDS, args, stream);
+    return launch<fa_fwd_f32_kernel<D, CAUSAL, MODE>>(nwg, F32Cfg<D>::LDS, args, stream);
 }
 
-template <typename E, int D, bool SPLIT>
+template <typename E, int D, int MODE>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     if (causal)
-        return launch<fa_fwd_mfma_kernel<E, D, true, SPLIT>>(nwg, 0, args, stream);
-    return launch<fa_fwd_mfma_kernel<E, D, false, SPLIT>>(nwg, 0, args, stream);
+        return launch<fa_fwd_mfma_kernel<E, D, true, MODE>>(nwg, 0, args, stream);
+    return launch<fa_fwd_mfma_kernel<E, D, false, MODE>>(nwg, 0, args, stream);
 }
 
-template <bool SPLIT>
+template <int MODE>
 hipError_t launch_dtype(int dtype, int D, bool causal, int64_t nwg, const FwdArgs &args,
                         hipStream_t stream) {
     if (dtype == 0) {
         if (D == 64)
-            return causal ? launch_f32<64, true, SPLIT>(nwg, args, stream)
-                          : launch_f32<64, false, SPLIT>(nwg, args, stream);
-        return causal ? launch_f32<128, true, SPLIT>(nwg, args, stream)
-                      : launch_f32<128, false, SPLIT>(nwg, args, stream);
+            return causal ? launch_f32<64, true, MODE>(nwg, args, stream)
+                          : launch_f32<64, false, MODE>(nwg, args, stream);
+        return causal ? launch_f32<128, true, MODE>(nwg, args, stream)
+                      : launch_f32<128, false, MODE>(nwg, args, stream);
     }
     if (dtype == 1)
-        return D == 64 ? launch_mfma<Bf16, 64, SPLIT>(causal, nwg, args, stream)
-                       : launch_mfma<Bf16, 128, SPLIT>(causal, nwg, args, stream);
-    return D == 64 ? launch_mfma<F16, 64, SPLIT>(causal, nwg, args, stream)
-                   : launch_mfma<F16, 128, SPLIT>(causal, nwg, args, stream);
+        return D == 64 ? launch_mfma<Bf16, 64, MODE>(causal, nwg, args, stream)
+                       : launch_mfma<Bf16, 128, MODE>(causal, nwg, args, stream);
+    return D == 64 ? launch_mfma<F16, 64, MODE>(causal, nwg, args, stream)
+                   : launch_mfma<F16, 128, MODE>(causal, nwg, args, stream);
 }
 
 } // namespace
 
-hipError_t launch_fwd(int dtype, int D, bool causal, bool split, int64_t BH, const FwdArgs &args,
-                      hipStream_t stream) {
-    // one workgroup per (slice, query block), times the key splits
-    const int64_t nwg = BH * (int64_t)args.n_qblk * (split ? args.n_splits : 1);
-    return split ? launch_dtype<true>(dtype, D, causal, nwg, args, stream)
-                 : launch_dtype<false>(dtype, D, causal, nwg, args, stream);
+hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
+                      const FwdArgs &args, hipStream_t stream) {
+    // one workgroup per (grid row, query block)
+    const int64_t nwg = rows * (int64_t)args.n_qblk;
+    if (mode == kSplit)
+        return launch_dtype<kSplit>(dtype, D, causal, nwg, args, stream);
+    if (mode == kVarlen)
+        return launch_dtype<kVarlen>(dtype, D, causal, nwg, args, stream);
+    return launch_dtype<kDense>(dtype, D, causal, nwg, args, stream);
 }
 
 } // namespace fa

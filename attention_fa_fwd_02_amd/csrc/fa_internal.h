@@ -24,16 +24,29 @@ struct FwdArgs {
     int64_t part_rows; // rows per split in part_o / part_lse: B * H * N
     int32_t split_keys; // a multiple of 128 (the key tile of every path)
     int32_t n_splits;
+    // packed variable-length launches only (ignored otherwise): q, o are
+    // [n_heads][total_q][D], k, v [n_heads][total_k][D], lse [n_heads][total_q];
+    // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    int32_t n_heads;
+    int32_t total_q;
+    int32_t total_k;
 };
+
+// Kernel modes: one (batch, head) slice per grid row; that plus key splits;
+// packed variable-length sequences.
+enum FwdMode { kDense = 0, kSplit = 1, kVarlen = 2 };
 
 // Query rows per workgroup for every path (8 waves x 32 rows).
 constexpr int kQueryBlock = 256;
 
-// Enqueue the forward pass; arguments are already validated.  With
-// split = true the grid covers args.n_splits key splits per query block and
-// writes part_o / part_lse instead of o / lse.
-hipError_t launch_fwd(int dtype, int D, bool causal, bool split, int64_t BH, const FwdArgs &args,
-                      hipStream_t stream);
+// Enqueue the forward pass; arguments are already validated.  `rows` is the
+// number of grid rows: B*H slices (kDense), B*H*n_splits (kSplit, which
+// writes part_o / part_lse instead of o / lse) or n_seqs*n_heads (kVarlen);
+// each row has args.n_qblk query blocks.
+hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
+                      const FwdArgs &args, hipStream_t stream);
 
 // Merge n_parts partial results per row: part_o [n_parts][rows][D] fp32,
 // part_lse [n_parts][rows]; writes o [rows][D] (dtype 0 fp32, 1 bf16, 2 fp16)

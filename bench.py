@@ -211,6 +211,52 @@ def bench_one(name, steps, warmup, copy_calibration=False):
     return res, (host, (o, lse), B, H, N, D, dtype, causal)
 
 
+def bench_varlen(name, steps, warmup):
+    """The packed length-mix workload through fa_fwd_varlen (stderr line only)."""
+    import numpy as np
+    import torch
+
+    import attention_fa_fwd_02_amd as fa
+    import fa_inputs as fi
+    causal = name.endswith("causal")
+    w = fi.VARLEN_WORKLOAD
+    lens = fi.make_seqlens(w["n_seqs"], w["lo"], w["hi"], w["seed"])
+    cu = fi.cu_seqlens(lens)
+    H, D, dtype = w["H"], w["D"], w["dtype"]
+    total = int(cu[-1])
+    q, k, v = fi.make_packed(H, total, total, D, dtype, w["seed"], *w["sigma"])
+    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    dq, dk, dv = up(q), up(k), up(v)
+    dcu = torch.from_numpy(cu).to("cuda")
+    o = torch.empty_like(dq)
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(D)
+    max_len = int(lens.max())
+
+    def step():
+        st = fa.fa_fwd_varlen(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              dcu.data_ptr(), dcu.data_ptr(), len(lens), H, total, total, max_len, D, scale,
+                              int(causal), fa.FA_DTYPE_BF16, stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_fwd_varlen")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flops = fi.varlen_flops(lens, lens, H, D, causal)
+    log("%s: %d packed sequences (%d..%d rows, %d total) H%d D%d bf16 causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of bf16 peak"
+        % (name, len(lens), int(lens.min()), max_len, total, H, D, causal, ms, flops / (ms * 1e-3) / 1e12,
+           100 * flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +285,8 @@ def main():
         for name in list(WORKLOADS) + list(SPLIT_WORKLOADS):
             if name != args.workload:
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
+        for name in ("varlen", "varlen_causal"):
+            bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     r = main_res
     if not args.no_cpu_baseline:
         r["cpu_baseline"] = cpu_baseline(*main_ctx)

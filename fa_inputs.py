@@ -71,6 +71,28 @@ def make_qkv(B: int, H: int, N: int, D: int, dtype: str, seed: int,
     return q, k, v
 
 
+def make_seqlens(n_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths for a packed batch: n_seqs integers drawn uniformly from
+    [lo, hi] (PCG64 seeded with ``seed``)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi, size=n_seqs, endpoint=True).astype(np.int64)
+
+
+def cu_seqlens(lens) -> np.ndarray:
+    """Start row of every sequence plus the total: [0, l0, l0 + l1, ...] (int32)."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+def make_packed(H: int, total_q: int, total_k: int, D: int, dtype: str, seed: int,
+                sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0):
+    """Head-major packed Q [H, total_q, D], K and V [H, total_k, D], drawn like make_qkv."""
+    ss = np.random.SeedSequence(seed).spawn(3)
+    q = _draw(np.random.Generator(np.random.PCG64(ss[0])), (H, total_q, D), sigma_q, dtype)
+    k = _draw(np.random.Generator(np.random.PCG64(ss[1])), (H, total_k, D), sigma_k, dtype)
+    v = _draw(np.random.Generator(np.random.PCG64(ss[2])), (H, total_k, D), sigma_v, dtype)
+    return q, k, v
+
+
 def sample_rows(N: int, n_rows: int, seed: int) -> np.ndarray:
     """Sorted query positions: 0 and N-1 always, the rest drawn without replacement."""
     if n_rows >= N:
@@ -107,7 +129,19 @@ WORKLOADS = {
 }
 
 
+# Packed variable-length batch: 16 sequences of lengths drawn uniformly from
+# [128, 4096] (self-attention, n_q = n_k per sequence), 16 heads, D = 128.
+VARLEN_WORKLOAD = dict(n_seqs=16, lo=128, hi=4096, H=16, D=128, dtype="bf16", seed=1007,
+                       sigma=(1.0, 1.0, 1.0))
+
+
 def workload_flops(B: int, H: int, N: int, D: int, causal: bool) -> float:
     """The metric's FLOP count: 4*B*H*N^2*D, halved for causal."""
     f = 4.0 * B * H * N * N * D
+    return f / 2 if causal else f
+
+
+def varlen_flops(lens_q, lens_k, H: int, D: int, causal: bool) -> float:
+    """4*H*D*sum_b n_q(b)*n_k(b), halved for causal (the dense metric's convention)."""
+    f = 4.0 * H * D * float(np.sum(np.asarray(lens_q, np.float64) * np.asarray(lens_k, np.float64)))
     return f / 2 if causal else f

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version",
                           "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
-                          "fa_lse_merge"}
+                          "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -207,3 +207,57 @@ def test_merge_invalid_arguments(kw):
                                 dict(P=1024, rows=1 << 24, D=512)])
 def test_merge_unsupported(kw):
     assert merge_call(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ packed sequences
+
+VQ, VK, VV, VO, VL, CQ, CK = (T * i for i in range(1, 8))
+VGOOD = dict(q=VQ, k=VK, v=VV, o=VO, lse=VL, cq=CQ, ck=CK, n=3, H=4, tq=1000, tk=1200, maxq=500, D=128,
+             scale=0.1, causal=1, dtype=1)
+
+
+def vcheck(arch="gfx950", **kw):
+    a = dict(VGOOD)
+    a.update(kw)
+    return fa.fa_check_varlen_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["n"], a["H"],
+                                   a["tq"], a["tk"], a["maxq"], a["D"], a["scale"], a["causal"], a["dtype"], arch)
+
+
+def test_varlen_good_arguments_pass():
+    assert vcheck() == fa.FA_OK
+    assert vcheck(arch=None) == fa.FA_OK
+    for dt in (0, 1, 2):
+        for D in (64, 128):
+            for c in (0, 1):
+                assert vcheck(dtype=dt, D=D, causal=c) == fa.FA_OK
+    assert vcheck(maxq=1000) == fa.FA_OK and vcheck(n=1, maxq=1) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0), dict(cq=0), dict(ck=0),
+    dict(n=0), dict(H=0), dict(tq=0), dict(tk=0), dict(D=0), dict(maxq=0), dict(maxq=1001),
+    dict(scale=float("nan")), dict(causal=2), dict(dtype=5),
+    dict(q=VQ + 8), dict(o=VO + 4), dict(lse=VL + 2), dict(cq=CQ + 2), dict(ck=CK + 1),
+    dict(o=VQ + 256), dict(o=VK - 256), dict(lse=VV + 64), dict(lse=CQ), dict(o=CK - 16), dict(lse=VO + 1024),
+])
+def test_varlen_invalid_arguments(kw):
+    assert vcheck(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(D=96), dict(D=256), dict(tq=1 << 30, maxq=100), dict(tk=1 << 30), dict(H=1 << 20),
+    dict(H=1 << 12, tq=1 << 24, maxq=100), dict(n=1 << 13, H=1 << 8, maxq=1000, tq=1 << 20),
+])
+def test_varlen_unsupported(kw):
+    assert vcheck(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_unsupported_arch():
+    assert vcheck(arch="gfx942") == fa.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_reports_invalid_args_before_any_hip_call():
+    st = fa.fa_fwd_varlen(VQ, VK, VV, VO, VL, 0, CK, 3, 4, 1000, 1200, 500, 128, 0.1, 1, 1, 0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    st = fa.fa_fwd_varlen(VQ, VK, VV, VO, VL, CQ, CK, 3, 4, 1000, 1200, 500, 80, 0.1, 1, 1, 0)
+    assert st == fa.FA_ERR_UNSUPPORTED
