@@ -69,6 +69,12 @@ def _load():
             ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int,
         ]
+        lib.oracle_attention_bwd.restype = ctypes.c_int
+        lib.oracle_attention_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -191,6 +197,31 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, n_threads:
                                               causal, n_threads, causal_offset=(k1 - k0) - (q1 - q0))
         out.append((b, rows, o, lse))
     return out
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, n_threads: int = 0):
+    """Gradients (dQ, dK, dV) in fp64 of the square attention forward for the
+    output gradient dout; [..., N, D] arrays, leading dims independent slices.
+    The definition (explicit P, softmax Jacobian) is in oracle.c."""
+    lib = _load()
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    if not (q.shape == k.shape == v.shape == dout.shape) or q.ndim < 2:
+        raise ValueError("q, k, v, dout must share one [..., N, D] shape")
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    flat = [np.ascontiguousarray(x.reshape(-1, n, d)) for x in (q, k, v, dout)]
+    outs = [np.empty_like(flat[0]) for _ in range(3)]
+    for s in range(flat[0].shape[0]):
+        rc = lib.oracle_attention_bwd(flat[0][s].ctypes.data, flat[1][s].ctypes.data, flat[2][s].ctypes.data,
+                                      flat[3][s].ctypes.data, n, d, float(scale), int(bool(causal)),
+                                      outs[0][s].ctypes.data, outs[1][s].ctypes.data, outs[2][s].ctypes.data,
+                                      int(n_threads))
+        if rc != 0:
+            raise ValueError("oracle_attention_bwd failed with code %d" % rc)
+    return tuple(x.reshape(*lead, n, d) for x in outs)
 
 
 def lse_merge(part_o, part_lse):

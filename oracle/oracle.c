@@ -183,3 +183,115 @@ int oracle_attention_rows(const double *q_rows, const double *k, const double *v
     return oracle_attention_rows_range(q_rows, k, v, n_keys, d, row_index, n_rows, 0, n_keys,
                                        scale, causal, o_rows, lse_rows, n_threads);
 }
+
+/*
+ * Gradients of one square (batch, head) slice, for a loss whose gradient
+ * with respect to O is dout ("dO"):
+ *
+ *   P        = softmax rows of S = scale * Q K^T (causal: keys j <= i), as above
+ *   dV       = P^T dO
+ *   dP       = dO V^T
+ *   Delta_i  = sum_j P[i][j] * dP[i][j]
+ *   dS[i][j] = P[i][j] * (dP[i][j] - Delta_i)        (softmax Jacobian)
+ *   dQ       = scale * dS K
+ *   dK       = scale * dS^T Q
+ *
+ * The pages describe the backward pass only as recomputing P from the saved
+ * O and row statistics instead of storing it ("08 · FlashAttention", part 3,
+ * on the backward pass); the gradient itself is the derivative of the
+ * forward definition, written out here with an explicit P matrix.
+ *   q, k, v, dout  [n, d]   one slice (fp64)
+ *   dq, dk, dv     [n, d]   outputs (fp64)
+ * Returns 0 on success, 1 on an invalid argument, 2 if memory ran out.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dout,
+                         int64_t n, int64_t d, double scale, int causal, double *dq, double *dk,
+                         double *dv, int n_threads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return 1;
+    if (n < 1 || d < 1 || (causal != 0 && causal != 1) || !isfinite(scale))
+        return 1;
+    double *P = (double *)malloc((size_t)n * (size_t)n * sizeof(double));
+    double *dS = (double *)malloc((size_t)n * (size_t)n * sizeof(double));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return 2;
+    }
+#ifdef _OPENMP
+    int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#else
+    (void)n_threads;
+#endif
+    /* forward: P row by row (explicit scores, three passes); masked entries are 0 */
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+    for (int64_t i = 0; i < n; i++) {
+        double *Pi = P + i * n;
+        const int64_t n_vis = causal ? i + 1 : n;
+        for (int64_t j = 0; j < n; j++) {
+            if (j >= n_vis) {
+                Pi[j] = 0.0;
+                continue;
+            }
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; c++)
+                dot += q[i * d + c] * k[j * d + c];
+            Pi[j] = scale * dot;
+        }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n_vis; j++)
+            if (Pi[j] > m)
+                m = Pi[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < n_vis; j++)
+            l += exp(Pi[j] - m);
+        for (int64_t j = 0; j < n_vis; j++)
+            Pi[j] = exp(Pi[j] - m) / l;
+    }
+    /* dP, Delta and dS row by row; dQ = scale * dS K */
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+    for (int64_t i = 0; i < n; i++) {
+        const double *Pi = P + i * n;
+        double *dSi = dS + i * n;
+        for (int64_t j = 0; j < n; j++) {
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; c++)
+                dp += dout[i * d + c] * v[j * d + c];
+            dSi[j] = dp; /* dP for now */
+        }
+        double delta = 0.0;
+        for (int64_t j = 0; j < n; j++)
+            delta += Pi[j] * dSi[j];
+        for (int64_t j = 0; j < n; j++)
+            dSi[j] = Pi[j] * (dSi[j] - delta);
+        for (int64_t c = 0; c < d; c++) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; j++)
+                acc += dSi[j] * k[j * d + c];
+            dq[i * d + c] = scale * acc;
+        }
+    }
+    /* dV = P^T dO and dK = scale * dS^T Q, key by key */
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+    for (int64_t j = 0; j < n; j++) {
+        for (int64_t c = 0; c < d; c++) {
+            double av = 0.0, ak = 0.0;
+            for (int64_t i = 0; i < n; i++) {
+                av += P[i * n + j] * dout[i * d + c];
+                ak += dS[i * n + j] * q[i * d + c];
+            }
+            dv[j * d + c] = av;
+            dk[j * d + c] = scale * ak;
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}
