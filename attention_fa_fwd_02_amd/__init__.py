@@ -7,10 +7,12 @@ device is not gfx950 the calls raise.
 
 Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
 ``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
-``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_status_string``,
-``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen`` and ``lse_merge``
-are convenience wrappers that allocate outputs (and the split workspace) with
-torch (device memory and the current stream are all torch provides).
+``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_bwd``,
+``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_status_string``,
+``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen``, ``bwd`` and
+``lse_merge`` are convenience wrappers that allocate outputs (and
+workspaces) with torch (device memory and the current stream are all torch
+provides).
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INV
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_MAX_SPLITS", "FaError", "lib_path",
            "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
-           "fa_status_string", "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "lse_merge"]
+           "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_status_string",
+           "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "bwd", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -73,6 +76,14 @@ def load_library():
         lib.fa_check_varlen_args.restype = ctypes.c_int
         lib.fa_check_varlen_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_char_p]
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                          vp, ctypes.c_uint64, vp]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_uint64
+        lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.fa_check_bwd_args.restype = ctypes.c_int
+        lib.fa_check_bwd_args.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                                     ctypes.c_int, vp, ctypes.c_uint64, ctypes.c_char_p]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -141,6 +152,28 @@ def fa_check_varlen_args(q: int, k: int, v: int, o: int, lse: int, cu_q: int, cu
     a = arch.encode() if arch is not None else None
     return int(load_library().fa_check_varlen_args(q, k, v, o, lse, cu_q, cu_k, n_seqs, H, total_q,
                                                    total_k, max_seqlen_q, D, scale, causal, dtype, a))
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, B: int, H: int,
+           N: int, D: int, scale: float, causal: int, dtype: int, workspace: int, workspace_bytes: int,
+           stream: int) -> int:
+    """Raw C call with integer device addresses; returns the fa_status code."""
+    return int(load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, causal, dtype,
+                                     workspace, workspace_bytes, stream))
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, D: int) -> int:
+    """Workspace bytes fa_bwd needs (0 for invalid arguments); host only."""
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, D))
+
+
+def fa_check_bwd_args(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, B: int,
+                      H: int, N: int, D: int, scale: float, causal: int, dtype: int, workspace: int,
+                      workspace_bytes: int, arch: str | None = None) -> int:
+    """Host-only argument check of fa_bwd (no HIP call); returns the fa_status code."""
+    a = arch.encode() if arch is not None else None
+    return int(load_library().fa_check_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, causal,
+                                                dtype, workspace, workspace_bytes, a))
 
 
 def _dtype_code(t) -> int:
@@ -276,6 +309,37 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: fl
     if st != FA_OK:
         raise FaError(st, "fa_fwd_varlen")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False, stream=None):
+    """(dQ, dK, dV) of the forward pass that produced o and lse (fa_bwd); all
+    [B, H, N, D] CUDA tensors of one 16-bit dtype, lse float32 [B, H, N]."""
+    import torch
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must all be [B, H, N, D] with the same shape")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError("%s is not a device tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    B, H, N, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa_bwd_workspace_bytes(B, H, N, D)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, float(scale), int(bool(causal)),
+                    _dtype_code(q.dtype), ws.data_ptr(), ws.numel(), handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def lse_merge(part_o, part_lse, out_dtype=None, out=None, lse=None, stream=None):

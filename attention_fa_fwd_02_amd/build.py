@@ -10,8 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
-           os.path.join(CSRC, "fa_merge.hip")]
-HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(ROOT, "include", "fa.h")]
+           os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_bwd.hip")]
+HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(CSRC, "fa_device.h"),
+           os.path.join(ROOT, "include", "fa.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

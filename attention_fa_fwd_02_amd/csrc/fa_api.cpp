@@ -292,6 +292,92 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
+    if (B < 1 || H < 1 || N < 1 || D < 1)
+        return 0;
+    uint64_t x = 0;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &x) || !mul_ok(x, (uint64_t)N, &x) || !mul_ok(x, 4u, &x))
+        return 0;
+    return x;
+}
+
+fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                            const float *lse, const void *dq, const void *dk, const void *dv, int64_t B,
+                            int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
+                            const void *workspace, uint64_t workspace_bytes, const char *arch) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || D < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || (causal != 0 && causal != 1))
+        return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+        return FA_ERR_INVALID_ARG;
+    if ((uintptr_t)lse & 3u)
+        return FA_ERR_INVALID_ARG;
+    if (dtype == FA_DTYPE_F32 || (D != 64 && D != 128))
+        return FA_ERR_UNSUPPORTED;
+    if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
+        return FA_ERR_UNSUPPORTED;
+    const int64_t BH = B * H;
+    if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
+        return FA_ERR_UNSUPPORTED;
+    if (BH * ((N + 127) / 128) >= (int64_t(1) << 23))
+        return FA_ERR_UNSUPPORTED;
+    const uint64_t need = fa_bwd_workspace_bytes(B, H, N, D);
+    if (workspace_bytes < need)
+        return FA_ERR_INVALID_ARG;
+    const uint64_t tbytes = (uint64_t)(BH * N * D) * elem_size(dtype);
+    const uint64_t lbytes = (uint64_t)(BH * N) * 4u;
+    const void *ins[6] = {q, k, v, o, dout, lse};
+    const uint64_t in_bytes[6] = {tbytes, tbytes, tbytes, tbytes, tbytes, lbytes};
+    const void *outs[4] = {dq, dk, dv, workspace};
+    const uint64_t out_bytes[4] = {tbytes, tbytes, tbytes, need};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+                return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+                return FA_ERR_INVALID_ARG;
+    }
+    if (arch && std::strncmp(arch, "gfx950", 6) != 0)
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t N, int64_t D,
+                 float scale, int causal, fa_dtype dtype, void *workspace, uint64_t workspace_bytes,
+                 fa_stream_t stream) {
+    fa_status st = fa_check_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, causal, (int)dtype,
+                                     workspace, workspace_bytes, nullptr);
+    if (st != FA_OK)
+        return st;
+    if ((st = check_device()) != FA_OK)
+        return st;
+    fa::BwdArgs args{};
+    args.q = q;
+    args.k = k;
+    args.v = v;
+    args.o = o;
+    args.dout = dout;
+    args.lse = lse;
+    args.delta = (float *)workspace;
+    args.dq = dq;
+    args.dk = dk;
+    args.dv = dv;
+    args.N = (int32_t)N;
+    args.c2 = scale * 1.44269504088896340736f;
+    args.scale = scale;
+    const hipError_t err = fa::launch_bwd((int)dtype, (int)D, causal != 0, B * H, args,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_lse_merge(const float *part_o, const float *part_lse, int64_t n_parts, int64_t rows,
                        int64_t D, void *o, float *lse, fa_dtype dtype, fa_stream_t stream) {
     if (!part_o || !part_lse || !o || !lse)

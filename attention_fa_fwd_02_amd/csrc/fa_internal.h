@@ -48,6 +48,28 @@ constexpr int kQueryBlock = 256;
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
                       const FwdArgs &args, hipStream_t stream);
 
+// Backward-pass kernel arguments, passed by value.
+struct BwdArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *o;
+    const void *dout;
+    const float *lse;   // forward logsumexp (natural log), [B*H][N]
+    float *delta;       // workspace: Delta_i = dO_i . O_i, [B*H][N]
+    void *dq;
+    void *dk;
+    void *dv;
+    int32_t N;
+    float c2;           // scale * log2(e) (signed): P = exp2(c2 * q.k - log2(e) * lse)
+    float scale;        // dQ = scale * dS K, dK = scale * dS^T Q
+};
+
+// Enqueue the three backward kernels (Delta, dQ, dK/dV) for a [B*H] x N x D
+// problem; arguments are already validated.
+hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &args,
+                      hipStream_t stream);
+
 // Merge n_parts partial results per row: part_o [n_parts][rows][D] fp32,
 // part_lse [n_parts][rows]; writes o [rows][D] (dtype 0 fp32, 1 bf16, 2 fp16)
 // and lse [rows].  D is a multiple of 8.

@@ -23,7 +23,8 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, B4 H16 N4096 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense MFMA, published
-KERNEL_SRC = os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", "fa_fwd.hip")
+# the forward kernel's sources: the kernel file and the device helpers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_mfma_bf16_d128_B4H16N4096_counters.txt")
 
 WORKLOADS = {
@@ -49,7 +50,10 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def read_traffic():
@@ -257,6 +261,48 @@ def bench_varlen(name, steps, warmup):
            100 * flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"]))
 
 
+def bench_bwd(name, steps, warmup):
+    """fa_bwd on the headline shape (stderr line only).  FLOPs: the five
+    contractions of the backward pass, 10*B*H*N^2*D (2.5x the forward's count,
+    halved for causal); the kernels recompute S and dP once more (seven)."""
+    import torch
+
+    import attention_fa_fwd_02_amd as fa
+    import fa_inputs as fi
+    causal = name.endswith("causal")
+    B, H, N, D, dtype = 4, 16, 4096, 128, "bf16"
+    host, (q, k, v) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0))
+    _, (do, _, _) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0), seed=1004 + 7919)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsb = fa.fa_bwd_workspace_bytes(B, H, N, D)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, scale, int(causal),
+                       fa.FA_DTYPE_BF16, ws.data_ptr(), wsb, stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_bwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flops = 2.5 * fi.workload_flops(B, H, N, D, causal)
+    tf = flops / (ms * 1e-3) / 1e12
+    log("%s: B%d H%d N%d D%d bf16 causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of bf16 peak"
+        % (name, B, H, N, D, causal, ms, tf, 100 * tf / PEAK_TFLOPS["bf16"]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +333,8 @@ def main():
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("varlen", "varlen_causal"):
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
+        for name in ("bwd", "bwd_causal"):
+            bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     r = main_res
     if not args.no_cpu_baseline:
         r["cpu_baseline"] = cpu_baseline(*main_ctx)

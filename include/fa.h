@@ -260,6 +260,64 @@ fa_status fa_check_varlen_args(const void *q, const void *k, const void *v, cons
                                int64_t total_k, int64_t max_seqlen_q, int64_t D, float scale, int causal,
                                int dtype, const char *arch);
 
+/*
+ * Backward pass.  The forward pass keeps only O and lse; the backward pass
+ * recomputes P = exp(scale * q.k - lse) tile by tile on chip rather than
+ * reading a stored N x N matrix ("08 · FlashAttention", part 3, on the
+ * backward pass).  For an output gradient dO it computes
+ *   dV = P^T dO,  dP = dO V^T,  Delta_i = dO_i . O_i,  dS = P * (dP - Delta),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q
+ * (Delta_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j).
+ *
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs: B*H*N*4 bytes
+ * (Delta, fp32).  Returns 0 if an argument is < 1 or the size overflows.
+ * Host only.
+ */
+uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+
+/*
+ * fa_bwd -- enqueue the backward pass on `stream` (three kernels: Delta, dQ,
+ * dK/dV).
+ *
+ *   q, k, v, o, dout  device pointers, [B, H, N, D] of element type `dtype`,
+ *                     read-only: the forward inputs, its output O and the
+ *                     gradient of the loss with respect to O.
+ *   lse               device pointer, fp32 [B, H, N]: the forward logsumexp
+ *                     (as fa_fwd writes it) for the same q, k, scale, causal.
+ *   dq, dk, dv        device pointers, [B, H, N, D] of element type `dtype`;
+ *                     fully overwritten (fp32 accumulation, rounded to nearest
+ *                     even once).
+ *   workspace         device pointer, 16-byte aligned, at least
+ *                     fa_bwd_workspace_bytes(B, H, N, D) bytes; overwritten.
+ *   B, H, N, D, scale, causal, stream  as for fa_fwd.
+ *   dtype             FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32:
+ *                     FA_ERR_UNSUPPORTED in this build).
+ *
+ * Errors: FA_ERR_INVALID_ARG for a NULL pointer, B/H/N/D < 1, a non-finite
+ * scale, causal not 0/1, an unknown dtype, a tensor or the workspace not
+ * 16-byte aligned, lse not 4-byte aligned, workspace_bytes too small, or
+ * dq/dk/dv/workspace overlapping each other or any input;
+ * FA_ERR_UNSUPPORTED for fp32, D other than 64/128, the size limits of
+ * fa_fwd, B*H*ceil(N/128) >= 2^23, or a device that is not gfx950;
+ * FA_ERR_HIP when a device query or a launch fails.  All checks precede any
+ * HIP call; the library allocates nothing.  Every output is written by
+ * exactly one workgroup (no atomics), so results do not depend on scheduling.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t N, int64_t D,
+                 float scale, int causal, fa_dtype dtype, void *workspace, uint64_t workspace_bytes,
+                 fa_stream_t stream);
+
+/*
+ * fa_check_bwd_args -- the argument checks of fa_bwd on the host only (no
+ * HIP call; pointers are compared, never dereferenced).  `arch` as for
+ * fa_check_args.  Returns FA_OK or the status fa_bwd would return.
+ */
+fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                            const float *lse, const void *dq, const void *dk, const void *dv, int64_t B,
+                            int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
+                            const void *workspace, uint64_t workspace_bytes, const char *arch);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

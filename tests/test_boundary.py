@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version",
                           "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
-                          "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args"}
+                          "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args", "fa_bwd",
+                          "fa_bwd_workspace_bytes", "fa_check_bwd_args"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -260,4 +261,57 @@ def test_varlen_reports_invalid_args_before_any_hip_call():
     st = fa.fa_fwd_varlen(VQ, VK, VV, VO, VL, 0, CK, 3, 4, 1000, 1200, 500, 128, 0.1, 1, 1, 0)
     assert st == fa.FA_ERR_INVALID_ARG
     st = fa.fa_fwd_varlen(VQ, VK, VV, VO, VL, CQ, CK, 3, 4, 1000, 1200, 500, 80, 0.1, 1, 1, 0)
+    assert st == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ backward
+
+BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, BWS = (T * i for i in range(1, 11))
+BGOOD = dict(q=BQ, k=BK, v=BV, o=BO, do=BDO, lse=BL, dq=BDQ, dk=BDK, dv=BDV, B=2, H=3, N=500, D=128, scale=0.1,
+             causal=1, dtype=1, ws=BWS, wsb=2 * 3 * 500 * 4)
+
+
+def bcheck(arch="gfx950", **kw):
+    a = dict(BGOOD)
+    a.update(kw)
+    return fa.fa_check_bwd_args(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["B"], a["H"], a["N"], a["D"], a["scale"], a["causal"], a["dtype"], a["ws"],
+                                a["wsb"], arch)
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 3, 500, 128) == 2 * 3 * 500 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 3, 500, 128) == 0
+    assert fa.fa_bwd_workspace_bytes(1 << 40, 1 << 30, 1, 64) == 0
+
+
+def test_bwd_good_arguments_pass():
+    assert bcheck() == fa.FA_OK and bcheck(arch=None) == fa.FA_OK
+    for dt in (1, 2):
+        for D in (64, 128):
+            for c in (0, 1):
+                assert bcheck(dtype=dt, D=D, causal=c) == fa.FA_OK
+    assert bcheck(scale=0.0) == fa.FA_OK and bcheck(scale=-2.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(do=0), dict(lse=0), dict(dq=0), dict(dv=0), dict(ws=0), dict(B=0), dict(N=0), dict(D=0),
+    dict(scale=float("nan")), dict(causal=3), dict(dtype=4), dict(q=BQ + 2), dict(dk=BDK + 8), dict(ws=BWS + 4),
+    dict(lse=BL + 1), dict(wsb=2 * 3 * 500 * 4 - 1), dict(dq=BO + 64), dict(dk=BQ - 64), dict(dv=BL - 16),
+    dict(ws=BDO + 128), dict(dk=BDQ + 16), dict(ws=BDV - 1024),
+])
+def test_bwd_invalid_arguments(kw):
+    assert bcheck(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(D=96), dict(D=256), dict(N=1 << 30),
+                                dict(B=1 << 14, H=1 << 6, N=128 * 8, wsb=1 << 62)])
+def test_bwd_unsupported(kw):
+    assert bcheck(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_reports_invalid_args_before_any_hip_call():
+    st = fa.fa_bwd(0, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 128, 0.1, 1, 1, BWS, 12000, 0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    st = fa.fa_bwd(BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 128, 0.1, 1, 0, BWS, 12000, 0)
     assert st == fa.FA_ERR_UNSUPPORTED
