@@ -18,6 +18,14 @@ hipError_t g_arch_err[kMaxDevices];
 
 size_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
+// Head dims of the forward kernels: 64 and 128 for fp32; 64, 96, 128, 192 and
+// 256 for bf16 / fp16.
+bool fwd_head_dim_ok(int64_t D, int dtype) {
+    if (D == 64 || D == 128)
+        return true;
+    return dtype != FA_DTYPE_F32 && (D == 96 || D == 192 || D == 256);
+}
+
 bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
     const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
     return pa < pb + nb && pb < pa + na;
@@ -44,7 +52,7 @@ fa_status check_device() {
 }
 
 fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse, int64_t N,
-                      float scale, fa_dtype dtype) {
+                      int64_t D, float scale, fa_dtype dtype) {
     fa::FwdArgs args{};
     args.q = q;
     args.k = k;
@@ -52,7 +60,7 @@ fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, floa
     args.o = o;
     args.lse = lse;
     args.N = (int32_t)N;
-    args.n_qblk = (int32_t)((N + fa::kQueryBlock - 1) / fa::kQueryBlock);
+    args.n_qblk = (int32_t)((N + fa::query_block(D) - 1) / fa::query_block(D));
     const float log2e = 1.44269504088896340736f;
     // c > 0 always: for |scale| * log2(e) below 1e-30 every weight exp2(c*s - m) is
     // exactly 1.0f, the same as for scale = 0, and masked scores (-inf) give
@@ -90,9 +98,10 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim not 64/128, problem too large for one launch, too many "
-               "key splits or merge parts, merge head dim not a power of two in 8..512, or device "
-               "is not gfx950)";
+        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32 and the "
+               "backward pass), problem too large for one launch, too many "
+               "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
+               "device is not gfx950)";
     case FA_ERR_HIP:
         return "HIP runtime error (device query or kernel launch failed)";
     default:
@@ -117,7 +126,7 @@ fa_status fa_check_args(const void *q, const void *k, const void *v, const void 
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (D != 64 && D != 128)
+    if (!fwd_head_dim_ok(D, dtype))
         return FA_ERR_UNSUPPORTED;
     // size limits: rows per launch and bytes per tensor
     if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
@@ -125,8 +134,8 @@ fa_status fa_check_args(const void *q, const void *k, const void *v, const void 
     const int64_t BH = B * H;
     if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;
-    const int64_t n_qblk = (N + fa::kQueryBlock - 1) / fa::kQueryBlock;
-    // the dispatch grid is counted in work-items (32-bit): 512 per workgroup
+    const int64_t n_qblk = (N + fa::query_block(D) - 1) / fa::query_block(D);
+    // the dispatch grid is counted in work-items (32-bit): up to 512 per workgroup
     if (BH * n_qblk >= (int64_t(1) << 23))
         return FA_ERR_UNSUPPORTED;
     const uint64_t tbytes = (uint64_t)(BH * N * D) * elem_size(dtype);
@@ -149,7 +158,7 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
         return st;
     if ((st = check_device()) != FA_OK)
         return st;
-    const fa::FwdArgs args = make_args(q, k, v, o, lse, N, scale, dtype);
+    const fa::FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
     const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kDense, B * H, args,
                                           reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -168,7 +177,7 @@ uint64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
 int64_t fa_fwd_split_choose(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int64_t n_cus) {
     if (B < 1 || H < 1 || N < 1 || D < 1 || n_cus < 1 || (causal != 0 && causal != 1))
         return 0;
-    const uint64_t n_qblk = ((uint64_t)N + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    const uint64_t n_qblk = ((uint64_t)N + fa::query_block(D) - 1) / fa::query_block(D);
     uint64_t wgs = 0;
     if (!mul_ok((uint64_t)B, (uint64_t)H, &wgs) || !mul_ok(wgs, n_qblk, &wgs) || wgs >= (uint64_t)n_cus)
         return 1; // the grid already has a workgroup for every compute unit
@@ -204,13 +213,13 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
         overlaps(workspace, need, v, tbytes) || overlaps(workspace, need, o, tbytes) ||
         overlaps(workspace, need, lse, lbytes))
         return FA_ERR_INVALID_ARG;
-    const int64_t n_qblk = (N + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    const int64_t n_qblk = (N + fa::query_block(D) - 1) / fa::query_block(D);
     if (BH * n_qblk * n_splits >= (int64_t(1) << 23))
         return FA_ERR_UNSUPPORTED;
     if ((st = check_device()) != FA_OK)
         return st;
 
-    fa::FwdArgs args = make_args(q, k, v, o, lse, N, scale, dtype);
+    fa::FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
     const int64_t rows = BH * N;
     args.part_o = (float *)workspace;
     args.part_lse = (float *)((char *)workspace + (uint64_t)n_splits * (uint64_t)rows * (uint64_t)D * 4u);
@@ -244,14 +253,14 @@ fa_status fa_check_varlen_args(const void *q, const void *k, const void *v, cons
         return FA_ERR_INVALID_ARG;
     if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
         return FA_ERR_INVALID_ARG;
-    if (D != 64 && D != 128)
+    if (!fwd_head_dim_ok(D, dtype))
         return FA_ERR_UNSUPPORTED;
     if (total_q >= (int64_t(1) << 30) || total_k >= (int64_t(1) << 30) || n_seqs >= (int64_t(1) << 30) ||
         H >= (int64_t(1) << 20))
         return FA_ERR_UNSUPPORTED;
     if (H * total_q >= (int64_t(1) << 36) || H * total_k >= (int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;
-    const int64_t n_qblk = (max_seqlen_q + fa::kQueryBlock - 1) / fa::kQueryBlock;
+    const int64_t n_qblk = (max_seqlen_q + fa::query_block(D) - 1) / fa::query_block(D);
     if (n_seqs * H * n_qblk >= (int64_t(1) << 23))
         return FA_ERR_UNSUPPORTED;
     const uint64_t qbytes = (uint64_t)(H * total_q * D) * elem_size(dtype);
@@ -280,8 +289,8 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
         return st;
     if ((st = check_device()) != FA_OK)
         return st;
-    fa::FwdArgs args = make_args(q, k, v, o, lse, 0, scale, dtype);
-    args.n_qblk = (int32_t)((max_seqlen_q + fa::kQueryBlock - 1) / fa::kQueryBlock);
+    fa::FwdArgs args = make_args(q, k, v, o, lse, 0, D, scale, dtype);
+    args.n_qblk = (int32_t)((max_seqlen_q + fa::query_block(D) - 1) / fa::query_block(D));
     args.cu_q = cu_seqlens_q;
     args.cu_k = cu_seqlens_k;
     args.n_heads = (int32_t)H;
@@ -388,7 +397,7 @@ fa_status fa_lse_merge(const float *part_o, const float *part_lse, int64_t n_par
         return FA_ERR_INVALID_ARG;
     if ((((uintptr_t)part_o | (uintptr_t)o) & 15u) || (((uintptr_t)part_lse | (uintptr_t)lse) & 3u))
         return FA_ERR_INVALID_ARG;
-    if (n_parts > 1024 || D < 8 || D > 512 || (D & (D - 1)) != 0)
+    if (n_parts > 1024 || D < 8 || D > 512 || (D % 8) != 0)
         return FA_ERR_UNSUPPORTED;
     if (rows >= (int64_t(1) << 40) || n_parts * rows * D >= (int64_t(1) << 40))
         return FA_ERR_UNSUPPORTED;

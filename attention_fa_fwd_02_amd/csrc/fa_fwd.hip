@@ -163,7 +163,13 @@ __device__ __forceinline__ SeqSlice seq_slice(const FwdArgs &a, int row, int D) 
 // ----------------------------------------------------------------------------
 template <int D>
 struct MfmaCfg {
-    static constexpr int BC = 128;                  // keys per tile
+    // waves per workgroup (32 query rows each): 8, or 4 when D > 192 so that a
+    // wave may use the whole register file of its SIMD
+    static constexpr int WAVES = D > 192 ? 4 : 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int QBLK = 32 * WAVES;         // query rows per workgroup
+    // keys per tile: 128, or 64 when D > 128 (a tile stays within 32 KB)
+    static constexpr int BC = D > 128 ? 64 : 128;
     static constexpr int KP = 2 * D + 16;           // K row pitch in LDS (bytes)
     static constexpr int VP = 2 * D + 32;           // V row pitch in LDS (bytes)
     // tiles arrive by direct-to-LDS loads: one instruction fills 1 KB (64 lanes x
@@ -173,9 +179,9 @@ struct MfmaCfg {
     static_assert(NK * 1024 == BC * KP && NV * 1024 == BC * VP, "tiles are whole 1 KB blocks");
     // every wave issues the same number of loads per tile, so that the number in
     // flight is a compile-time constant; the spare blocks land past the V region
-    static constexpr int LPW = (NK + NV + kWaves - 1) / kWaves; // loads per wave and tile
+    static constexpr int LPW = (NK + NV + WAVES - 1) / WAVES; // loads per wave and tile
     static constexpr int KST = BC * KP;
-    static constexpr int STAGE = 1024 * kWaves * LPW;
+    static constexpr int STAGE = 1024 * WAVES * LPW;
     static_assert(KST + BC * VP <= STAGE, "K and V regions fit in a stage");
     static constexpr int OP = 2 * D + 16;           // O staging row pitch (bytes)
     static constexpr int STAGES = 2;
@@ -184,9 +190,10 @@ struct MfmaCfg {
 };
 
 template <typename E, int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
     using Cfg = MfmaCfg<D>;
+    constexpr int W = Cfg::WAVES, QBLK = Cfg::QBLK;
     constexpr int BC = Cfg::BC;
     constexpr int KB = BC / 32; // 32-key MFMA blocks per tile
     constexpr int DC = D / 16;  // k-steps of the score MFMA
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     uint16_t *__restrict__ O = (uint16_t *)a.o + q_off;
     float *__restrict__ LSE = a.lse + lse_off;
 
-    const int q0 = wk.qb * kQueryBlock;
+    const int q0 = wk.qb * QBLK;
     const int q0w = q0 + 32 * wave; // first query row of this wave
     const int qi = q0w + r;         // this lane's query row
     if (VARLEN && q0 >= Nq) // the grid covers the longest sequence
@@ -237,21 +244,21 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
     // keys [k_begin, kv_end): the split's range (whole key tiles) cut at the
     // last key any row of the block sees
     const int k_begin = SPLIT ? split * a.split_keys : 0;
-    const int kv_vis = CAUSAL ? min(Nk, q0 + kQueryBlock + coff) : Nk;
+    const int kv_vis = CAUSAL ? min(Nk, q0 + QBLK + coff) : Nk;
     const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
     const int n_tiles = (SPLIT || VARLEN) ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
                                           : (kv_end + BC - 1) / BC;
     if constexpr (SPLIT) {
         float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * a.N;
         if (n_tiles == 0) { // no key of this split is visible to the block
-            if (tid < kQueryBlock && q0 + tid < Nq)
+            if (tid < QBLK && q0 + tid < Nq)
                 PLSE[q0 + tid] = -INFINITY;
             return;
         }
     }
     if constexpr (VARLEN) {
         if (n_tiles == 0) { // no key is visible to any row of the block: O = 0, lse = -inf
-            if (tid < kQueryBlock && q0 + tid < Nq) {
+            if (tid < QBLK && q0 + tid < Nq) {
                 const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int c = 0; c < D / 8; ++c)
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         voff2[j] = 0u;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-        const int blk = wave + kWaves * j;
+        const int blk = wave + W * j;
         const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
         const int pitch = is_k ? KP : VP;
         const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
@@ -304,10 +311,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
             __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D * 2)); // uniform
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int blk = wave + kWaves * j; // wave-uniform
+            const int blk = wave + W * j; // wave-uniform
             const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
             load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, off,
-                        st + 1024 * (wave + kWaves * j));
+                        st + 1024 * (wave + W * j));
         }
     };
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -482,34 +489,49 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_mfma_kernel(FwdArgs a) {
         // and m = -inf: O = 0, lse = -inf
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
-        static_assert(4 * 32 * OP4 <= Cfg::STAGE, "four waves' fp32 O rows fit in one stage");
         float *__restrict__ PO = a.part_o + (split * a.part_rows + (int64_t)bh * a.N) * D;
         float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * a.N;
-        tile_barrier();
-        lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4;
-        if (q0w < Nq) {
+        if constexpr (4 * 32 * OP4 <= Cfg::STAGE) {
+            tile_barrier();
+            lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4;
+            if (q0w < Nq) {
 #pragma unroll
-            for (int b = 0; b < OB; ++b)
+                for (int b = 0; b < OB; ++b)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
-                                     o[b][4 * a4 + 3] * inv};
-                    *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
+                                         o[b][4 * a4 + 3] * inv};
+                        *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
+                    }
+                if (g == 0 && qi < Nq)
+                    PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+            }
+            __syncthreads();
+            if (q0w < Nq) {
+                constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
+#pragma unroll
+                for (int j = 0; j < kChunks / 64; ++j) {
+                    const int ch = 64 * j + lane;
+                    const int row = ch / (D / 4), col = ch % (D / 4);
+                    const int q = q0w + row;
+                    const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
+                    if (q < Nq)
+                        *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
                 }
-            if (g == 0 && qi < Nq)
-                PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-        }
-        __syncthreads();
-        if (q0w < Nq) {
-            constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
+            }
+        } else {
+            // rows too wide to stage: 16-byte stores straight from the accumulators
+            if (q0w < Nq && qi < Nq) {
 #pragma unroll
-            for (int j = 0; j < kChunks / 64; ++j) {
-                const int ch = 64 * j + lane;
-                const int row = ch / (D / 4), col = ch % (D / 4);
-                const int q = q0w + row;
-                const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
-                if (q < Nq)
-                    *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
+                for (int b = 0; b < OB; ++b)
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
+                                         o[b][4 * a4 + 3] * inv};
+                        *(f32x4 *)(PO + (int64_t)qi * D + 32 * b + 8 * a4 + 4 * g) = w;
+                    }
+                if (g == 0)
+                    PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
             }
         }
         return;
@@ -770,7 +792,7 @@ constexpr int kMaxDevices = 64;
 
 // Dynamic LDS above 64 KB must be allowed once per kernel and device; each
 // kernel template instance gets its own flags.
-template <void (*Kernel)(FwdArgs)>
+template <void (*Kernel)(FwdArgs), int THREADS = kThreads>
 hipError_t launch(int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream) {
     if (lds > 64 * 1024) {
         static std::atomic<int> allowed[kMaxDevices];
@@ -787,7 +809,7 @@ hipError_t launch(int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream)
             allowed[dev].store(1, std::memory_order_release);
         }
     }
-    hipLaunchKernelGGL(Kernel, dim3((unsigned)nwg), dim3(kThreads), (size_t)lds, stream, args);
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)nwg), dim3(THREADS), (size_t)lds, stream, args);
     return hipGetLastError();
 }
 
@@ -799,9 +821,27 @@ hipError_t launch_f32(int64_t nwg, const FwdArgs &args, hipStream_t stream) {
 template <typename E, int D, int MODE>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
+    constexpr int T = MfmaCfg<D>::THREADS;
     if (causal)
-        return launch<fa_fwd_mfma_kernel<E, D, true, MODE>>(nwg, 0, args, stream);
-    return launch<fa_fwd_mfma_kernel<E, D, false, MODE>>(nwg, 0, args, stream);
+        return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
+    return launch<fa_fwd_mfma_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
+}
+
+// head dims of the 16-bit kernels
+template <typename E, int MODE>
+hipError_t launch_mfma_d(int D, bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
+    switch (D) {
+    case 64:
+        return launch_mfma<E, 64, MODE>(causal, nwg, args, stream);
+    case 96:
+        return launch_mfma<E, 96, MODE>(causal, nwg, args, stream);
+    case 128:
+        return launch_mfma<E, 128, MODE>(causal, nwg, args, stream);
+    case 192:
+        return launch_mfma<E, 192, MODE>(causal, nwg, args, stream);
+    default:
+        return launch_mfma<E, 256, MODE>(causal, nwg, args, stream);
+    }
 }
 
 template <int MODE>
@@ -815,10 +855,8 @@ hipError_t launch_dtype(int dtype, int D, bool causal, int64_t nwg, const FwdArg
                       : launch_f32<128, false, MODE>(nwg, args, stream);
     }
     if (dtype == 1)
-        return D == 64 ? launch_mfma<Bf16, 64, MODE>(causal, nwg, args, stream)
-                       : launch_mfma<Bf16, 128, MODE>(causal, nwg, args, stream);
-    return D == 64 ? launch_mfma<F16, 64, MODE>(causal, nwg, args, stream)
-                   : launch_mfma<F16, 128, MODE>(causal, nwg, args, stream);
+        return launch_mfma_d<Bf16, MODE>(D, causal, nwg, args, stream);
+    return launch_mfma_d<F16, MODE>(D, causal, nwg, args, stream);
 }
 
 } // namespace

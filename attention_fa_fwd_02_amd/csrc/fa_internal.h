@@ -13,7 +13,7 @@ struct FwdArgs {
     void *o;
     float *lse;
     int32_t N;      // keys = queries per (batch, head) slice
-    int32_t n_qblk; // query blocks per slice: ceil(N / kQueryBlock)
+    int32_t n_qblk; // query blocks per slice: ceil(N / query_block(D))
     float c;        // |scale| * log2(e): scores enter exp2 through one FMA
     uint32_t qneg;  // sign-bit mask XORed onto Q words when scale < 0 (0 otherwise)
     // key-split launches only (ignored otherwise): split s of slice bh covers
@@ -38,8 +38,11 @@ struct FwdArgs {
 // packed variable-length sequences.
 enum FwdMode { kDense = 0, kSplit = 1, kVarlen = 2 };
 
-// Query rows per workgroup for every path (8 waves x 32 rows).
+// Query rows per workgroup of the forward kernels for head dim D: 8 waves x
+// 32 rows, or 4 waves x 32 rows for D > 192 (the O accumulators and Q
+// operands then need the register file of one wave per SIMD).
 constexpr int kQueryBlock = 256;
+constexpr int query_block(int64_t D) { return D > 192 ? 128 : 256; }
 
 // Enqueue the forward pass; arguments are already validated.  `rows` is the
 // number of grid rows: B*H slices (kDense), B*H*n_splits (kSplit, which
@@ -72,7 +75,7 @@ hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &
 
 // Merge n_parts partial results per row: part_o [n_parts][rows][D] fp32,
 // part_lse [n_parts][rows]; writes o [rows][D] (dtype 0 fp32, 1 bf16, 2 fp16)
-// and lse [rows].  D is a multiple of 8.
+// and lse [rows].  D is a multiple of 8, at most 512.
 hipError_t launch_merge(int dtype, const float *part_o, const float *part_lse, int n_parts,
                         int64_t rows, int D, void *o, float *lse, hipStream_t stream);
 

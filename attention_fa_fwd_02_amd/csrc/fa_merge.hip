@@ -14,8 +14,8 @@
 //
 // Memory-bound: every partial element is read once and every output
 // element written once.  One lane handles 8 consecutive features of one row
-// (two 16-byte loads per part, one 16-byte store for 16-bit outputs), so a
-// wave covers 64 * 32 contiguous bytes of a part's rows per load.
+// (two 16-byte loads per part, one 16-byte store for 16-bit outputs), so the
+// lanes of a block cover whole consecutive rows of a part per load.
 #include "fa_internal.h"
 
 namespace fa {
@@ -40,19 +40,22 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
-// total = rows << d8_shift work items: item (row, c) merges features 8c..8c+7
+// One block handles rows_pb = 256 / (D/8) consecutive rows: thread t merges
+// features 8c .. 8c + 7 (c = t % (D/8)) of row t / (D/8); blocks stride over
+// the rows.
 template <int OUT>
 __global__ __launch_bounds__(kMergeThreads) void fa_merge_kernel(const float *__restrict__ part_o,
                                                                  const float *__restrict__ part_lse,
-                                                                 int n_parts, int64_t rows, int d8_shift,
+                                                                 int n_parts, int64_t rows, int D,
                                                                  void *__restrict__ o,
                                                                  float *__restrict__ lse) {
-    const int D = 8 << d8_shift;
-    const int64_t total = rows << d8_shift;
-    const int64_t stride = (int64_t)gridDim.x * kMergeThreads;
-    for (int64_t item = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x; item < total; item += stride) {
-        const int64_t row = item >> d8_shift;
-        const int c = (int)(item & ((1 << d8_shift) - 1));
+    const int d8 = D / 8;
+    const int rows_pb = kMergeThreads / d8;
+    const int t = threadIdx.x;
+    const int lr = t / d8, c = t - lr * d8;
+    if (lr >= rows_pb) // the last t % d8 threads of a block have no row
+        return;
+    for (int64_t row = (int64_t)blockIdx.x * rows_pb + lr; row < rows; row += (int64_t)gridDim.x * rows_pb) {
         float m = -INFINITY;
         for (int p = 0; p < n_parts; ++p)
             m = fmaxf(m, part_lse[p * rows + row]);
@@ -94,23 +97,20 @@ __global__ __launch_bounds__(kMergeThreads) void fa_merge_kernel(const float *__
 
 hipError_t launch_merge(int dtype, const float *part_o, const float *part_lse, int n_parts,
                         int64_t rows, int D, void *o, float *lse, hipStream_t stream) {
-    int d8_shift = 0;
-    while ((8 << d8_shift) < D)
-        ++d8_shift;
-    const int64_t total = rows << d8_shift;
+    const int rows_pb = kMergeThreads / (D / 8);
     // enough workgroups to fill the device several times over; the kernel
     // strides over the rest
-    const int64_t want = (total + kMergeThreads - 1) / kMergeThreads;
+    const int64_t want = (rows + rows_pb - 1) / rows_pb;
     const unsigned nwg = (unsigned)(want < (int64_t(1) << 16) ? want : (int64_t(1) << 16));
     if (dtype == 0)
         hipLaunchKernelGGL(fa_merge_kernel<0>, dim3(nwg), dim3(kMergeThreads), 0, stream, part_o,
-                           part_lse, n_parts, rows, d8_shift, o, lse);
+                           part_lse, n_parts, rows, D, o, lse);
     else if (dtype == 1)
         hipLaunchKernelGGL(fa_merge_kernel<1>, dim3(nwg), dim3(kMergeThreads), 0, stream, part_o,
-                           part_lse, n_parts, rows, d8_shift, o, lse);
+                           part_lse, n_parts, rows, D, o, lse);
     else
         hipLaunchKernelGGL(fa_merge_kernel<2>, dim3(nwg), dim3(kMergeThreads), 0, stream, part_o,
-                           part_lse, n_parts, rows, d8_shift, o, lse);
+                           part_lse, n_parts, rows, D, o, lse);
     return hipGetLastError();
 }
 

@@ -37,6 +37,10 @@ WORKLOADS = {
     "tiny_f32": (1, 1, 128, 64, "f32", False, (1.0, 1.0, 1.0)),
     "wide": (32, 32, 4096, 64, "bf16", False, (1.0, 1.0, 1.0)),
     "long_causal": (1, 8, 131072, 128, "bf16", True, (0.5, 0.5, 1.0)),
+    "d256": (4, 8, 4096, 256, "bf16", False, (1.0, 1.0, 1.0)),
+    "d256_causal": (4, 8, 4096, 256, "bf16", True, (1.0, 1.0, 1.0)),
+    "d96": (4, 16, 4096, 96, "bf16", False, (1.0, 1.0, 1.0)),
+    "d192": (4, 8, 4096, 192, "bf16", False, (1.0, 1.0, 1.0)),
     "few_heads": (1, 2, 8192, 128, "bf16", False, (1.0, 1.0, 1.0)),
     "few_heads_causal": (1, 2, 8192, 128, "bf16", True, (1.0, 1.0, 1.0)),
 }

@@ -61,8 +61,9 @@ typedef struct ihipStream_t *fa_stream_t;
  *            with the natural-log logsumexp of row n's scaled scores,
  *            ln sum_j exp(scale * q_n . k_j) over the visible keys j.
  *   B, H, N  >= 1.
- *   D        head dimension: 64 or 128 in this build (other values:
- *            FA_ERR_UNSUPPORTED).
+ *   D        head dimension: 64, 96, 128, 192 or 256 for bf16 / fp16; 64 or
+ *            128 for fp32 (other values: FA_ERR_UNSUPPORTED).  Up to 192 a
+ *            workgroup takes 256 query rows, above 192 it takes 128.
  *   scale    any finite float; usually 1/sqrt(D).  0 gives uniform weights.
  *   causal   0: every key visible; 1: key j visible to query i iff j <= i.
  *   dtype    FA_DTYPE_*.
@@ -76,9 +77,9 @@ typedef struct ihipStream_t *fa_stream_t;
  * FA_ERR_INVALID_ARG for a NULL pointer, B/H/N < 1, D < 1, a non-finite
  * scale, causal not 0/1, an unknown dtype, q/k/v/o not 16-byte aligned,
  * lse not 4-byte aligned, or o/lse overlapping each other or any input;
- * FA_ERR_UNSUPPORTED for D other than 64/128, a problem too large for one
- * launch (N >= 2^30, B*H*N >= 2^36 or B*H*ceil(N/256) >= 2^23), or a
- * current device that is not gfx950.  FA_ERR_HIP when a device query or
+ * FA_ERR_UNSUPPORTED for a head dim outside the list above, a problem too
+ * large for one launch (N >= 2^30, B*H*N >= 2^36, or B*H*ceil(N/R) >= 2^23
+ * with R the workgroup's query rows), or a current device that is not gfx950.  FA_ERR_HIP when a device query or
  * the launch fails.  The call returns without waiting for the kernel;
  * faults during execution surface at the caller's next synchronisation,
  * as usual for HIP.
@@ -135,7 +136,7 @@ uint64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D
 
 /*
  * fa_fwd_split_choose -- the split count this library would pick for a
- * device with n_cus compute units: 1 when B*H*ceil(N/256) workgroups already
+ * device with n_cus compute units: 1 when B*H*ceil(N/R) workgroups already
  * fill the device, else enough splits to give every compute unit one
  * workgroup, at most one split per eight key tiles (ceil(N/128) / 8: the
  * fp32 partials' round trip through memory must stay small next to a split's
@@ -164,7 +165,7 @@ int64_t fa_fwd_split_choose(int64_t B, int64_t H, int64_t N, int64_t D, int caus
  * Errors: the checks of fa_fwd, and FA_ERR_INVALID_ARG for n_splits < 1, a
  * NULL or misaligned workspace, workspace_bytes below the size needed, or a
  * workspace overlapping q, k, v, o or lse; FA_ERR_UNSUPPORTED for n_splits >
- * FA_MAX_SPLITS or B*H*ceil(N/256)*n_splits >= 2^23 workgroups.  All checks
+ * FA_MAX_SPLITS or B*H*ceil(N/R)*n_splits >= 2^23 workgroups (R as for fa_fwd).  All checks
  * are made before any HIP call.  The library allocates nothing.
  */
 fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -180,7 +181,7 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
  *   part_lse  device pointer, fp32 [n_parts][rows], 4-byte aligned; -inf
  *             marks an empty part (its part_o row is not read).
  *   n_parts   1 .. 1024.  rows >= 1.
- *   D         a power of two, 8 .. 512.
+ *   D         a multiple of 8, 8 .. 512.
  *   o         device pointer, [rows][D] of element type `dtype` (fp32, or
  *             bf16 / fp16 rounded to nearest even), 16-byte aligned;
  *             overwritten.  A row whose parts are all empty gets O = 0.
@@ -190,7 +191,7 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
  *
  * Errors: FA_ERR_INVALID_ARG for a NULL pointer, n_parts or rows < 1, a bad
  * dtype, misalignment, or o / lse overlapping each other or the partials;
- * FA_ERR_UNSUPPORTED for n_parts > 1024, D not a power of two in 8..512, or
+ * FA_ERR_UNSUPPORTED for n_parts > 1024, D not a multiple of 8 in 8..512, or
  * n_parts*rows*D >= 2^40; FA_ERR_HIP when a device query or the launch
  * fails.  Checks precede any HIP call; the library allocates nothing.
  */
@@ -239,9 +240,10 @@ fa_status fa_lse_merge(const float *part_o, const float *part_lse, int64_t n_par
  * total_k < 1, max_seqlen_q outside 1 .. total_q, a non-finite scale, causal
  * not 0/1, an unknown dtype, q/k/v/o not 16-byte aligned, lse or cu_seqlens
  * not 4-byte aligned, or o/lse overlapping each other or any input;
- * FA_ERR_UNSUPPORTED for D other than 64/128, total_q or total_k >= 2^30,
- * H >= 2^20, H*total >= 2^36, n_seqs*H*ceil(max_seqlen_q/256) >= 2^23, or a
- * device that is not gfx950; FA_ERR_HIP when a device query or the launch
+ * FA_ERR_UNSUPPORTED for a head dim fa_fwd does not support, total_q or
+ * total_k >= 2^30, H >= 2^20, H*total >= 2^36,
+ * n_seqs*H*ceil(max_seqlen_q/R) >= 2^23 (R as for fa_fwd), or a device that
+ * is not gfx950; FA_ERR_HIP when a device query or the launch
  * fails.  All checks precede any HIP call; the library allocates nothing.
  */
 fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,

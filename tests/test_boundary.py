@@ -44,6 +44,7 @@ def test_status_strings():
 
 # fake, well-separated, aligned device addresses: only compared, never dereferenced
 Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+T = 1 << 40  # address spacing for the large cases: no two tensors overlap
 GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, D=64, scale=0.125, causal=0, dtype=1)
 
 
@@ -79,11 +80,27 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(D=32), dict(D=96), dict(D=256), dict(N=1 << 30), dict(B=1 << 20, H=1 << 10, N=1 << 7),
-    dict(B=1 << 15, H=1 << 8, N=257),
+    dict(D=32), dict(D=80), dict(D=160), dict(D=512), dict(D=96, dtype=0), dict(D=256, dtype=0),
+    dict(N=1 << 30), dict(B=1 << 20, H=1 << 10, N=1 << 7), dict(B=1 << 15, H=1 << 8, N=257),
+    # head dims above 192 use 128-row query blocks: 2^16 * 2^7 blocks of 128 rows
+    dict(B=1 << 16, H=1 << 0, N=128 * 128, D=256, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T),
 ])
 def test_unsupported(kw):
     assert check(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [1, 2])
+@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
+def test_head_dims_16bit(D, dtype):
+    assert check(D=D, dtype=dtype) == fa.FA_OK
+
+
+def test_grid_limit_depends_on_query_block():
+    """2^22 query blocks of 256 rows pass at D = 128; the same N at D = 256 needs 2^23
+    blocks of 128 rows and is refused."""
+    big = dict(B=1 << 14, H=1 << 0, N=256 * 256, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T)
+    assert check(D=128, **big) == fa.FA_OK
+    assert check(D=256, **big) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_unsupported_arch():
@@ -167,11 +184,8 @@ def test_split_invalid_arguments(kw):
     assert split_call(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-T = 1 << 40  # address spacing for the large-grid case: no two tensors overlap
-
-
 @pytest.mark.parametrize("kw", [
-    dict(n_splits=65), dict(D=96),
+    dict(n_splits=65), dict(D=80), dict(D=96, dtype=0),
     # 2^22 workgroups pass fa_fwd's grid limit; two splits reach 2^23
     dict(B=1 << 12, H=1 << 8, N=1024, n_splits=2, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T, ws=6 * T,
          ws_bytes=1 << 62),
@@ -204,7 +218,7 @@ def test_merge_invalid_arguments(kw):
     assert merge_call(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(P=1025), dict(D=4), dict(D=96), dict(D=1024), dict(rows=1 << 40),
+@pytest.mark.parametrize("kw", [dict(P=1025), dict(D=4), dict(D=12), dict(D=520), dict(D=1024), dict(rows=1 << 40),
                                 dict(P=1024, rows=1 << 24, D=512)])
 def test_merge_unsupported(kw):
     assert merge_call(**kw) == fa.FA_ERR_UNSUPPORTED
@@ -246,7 +260,7 @@ def test_varlen_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(D=96), dict(D=256), dict(tq=1 << 30, maxq=100), dict(tk=1 << 30), dict(H=1 << 20),
+    dict(D=80), dict(D=512), dict(D=256, dtype=0), dict(tq=1 << 30, maxq=100), dict(tk=1 << 30), dict(H=1 << 20),
     dict(H=1 << 12, tq=1 << 24, maxq=100), dict(n=1 << 13, H=1 << 8, maxq=1000, tq=1 << 20),
 ])
 def test_varlen_unsupported(kw):

@@ -261,3 +261,19 @@ def test_side_stream_and_binding():
     torch.cuda.synchronize()
     assert torch.equal(o_ref.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l_ref, l2)
+
+
+# ---------------------------------------------------------------- head dims
+
+@pytest.mark.parametrize("N", [1, 100, 129, 300, 1000])
+@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims(N, D, dtype, causal):
+    check_case(2, 3, N, D, dtype, causal, seed=200 + N + D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_sampled(causal):
+    """B4 H8 N4096 D256 (the headline's FLOPs at twice the head dim): sampled rows."""
+    check_case(4, 8, 4096, 256, "bf16", causal, seed=1008, n_rows=128, row_seed=15)

@@ -124,6 +124,12 @@ def test_split_parity(N, n_splits, D, dtype, causal):
     check_split(2, 3, N, D, dtype, causal, n_splits, seed=300 + N + D)
 
 
+@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_head_dims(D, causal):
+    check_split(2, 3, 1000, D, "bf16", causal, 3, seed=350 + D)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_split_small_workload(causal):
     """The small bf16 workload in four splits (64 workgroups x 4 fill 256 CUs; the
@@ -181,7 +187,7 @@ def _merge_inputs(P, rows, D, seed):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("D", [8, 64, 128, 512])
+@pytest.mark.parametrize("D", [8, 64, 96, 128, 192, 512])
 @pytest.mark.parametrize("P", [1, 3, 7])
 def test_merge_parity(out, D, P):
     import attention_fa_fwd_02_amd as fa

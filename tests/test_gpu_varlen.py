@@ -108,6 +108,12 @@ def test_varlen_cross(D, dtype, causal):
     check_varlen(MIX_Q, MIX_K, 2, D, dtype, causal, seed=600 + D)
 
 
+@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_head_dims(D, causal):
+    check_varlen(MIX_Q, MIX_K, 2, D, "bf16", causal, seed=650 + D)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_workload_sampled(causal):
     """The 16-sequence length mix (128..4096 keys, H16 D128 bf16): 48 rows per sequence."""
