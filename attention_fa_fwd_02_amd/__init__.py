@@ -8,7 +8,8 @@ device is not gfx950 the calls raise.
 Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
 ``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
 ``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_bwd``,
-``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_status_string``,
+``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_fwd_fp8``,
+``fa_fwd_fp8_workspace_bytes``, ``fa_check_fp8_args``, ``fa_status_string``,
 ``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen``, ``bwd`` and
 ``lse_merge`` are convenience wrappers that allocate outputs (and
 workspaces) with torch (device memory and the current stream are all torch
@@ -24,7 +25,8 @@ __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INV
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_MAX_SPLITS", "FaError", "lib_path",
            "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
-           "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_status_string",
+           "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
+           "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_status_string",
            "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "bwd", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
@@ -84,6 +86,14 @@ def load_library():
         lib.fa_check_bwd_args.restype = ctypes.c_int
         lib.fa_check_bwd_args.argtypes = [vp] * 9 + [i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                                      ctypes.c_int, vp, ctypes.c_uint64, ctypes.c_char_p]
+        f32 = ctypes.c_float
+        lib.fa_fwd_fp8.restype = ctypes.c_int
+        lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i64] * 4 + [f32] * 4 + [ctypes.c_int, vp, ctypes.c_uint64, vp]
+        lib.fa_fwd_fp8_workspace_bytes.restype = ctypes.c_uint64
+        lib.fa_fwd_fp8_workspace_bytes.argtypes = [i64] * 4
+        lib.fa_check_fp8_args.restype = ctypes.c_int
+        lib.fa_check_fp8_args.argtypes = [vp] * 5 + [i64] * 4 + [f32] * 4 + [ctypes.c_int, vp, ctypes.c_uint64,
+                                                                            ctypes.c_char_p]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -174,6 +184,28 @@ def fa_check_bwd_args(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: i
     a = arch.encode() if arch is not None else None
     return int(load_library().fa_check_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, scale, causal,
                                                 dtype, workspace, workspace_bytes, a))
+
+
+def fa_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int, scale: float,
+               q_descale: float, k_descale: float, v_descale: float, causal: int, workspace: int,
+               workspace_bytes: int, stream: int) -> int:
+    """Raw C call with integer device addresses; returns the fa_status code."""
+    return int(load_library().fa_fwd_fp8(q, k, v, o, lse, B, H, N, D, scale, q_descale, k_descale, v_descale,
+                                         causal, workspace, workspace_bytes, stream))
+
+
+def fa_fwd_fp8_workspace_bytes(B: int, H: int, N: int, D: int) -> int:
+    """Workspace bytes fa_fwd_fp8 needs (0 for invalid arguments); host only."""
+    return int(load_library().fa_fwd_fp8_workspace_bytes(B, H, N, D))
+
+
+def fa_check_fp8_args(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int, scale: float,
+                      q_descale: float, k_descale: float, v_descale: float, causal: int, workspace: int,
+                      workspace_bytes: int, arch: str | None = None) -> int:
+    """Host-only argument check of fa_fwd_fp8 (no HIP call); returns the fa_status code."""
+    a = arch.encode() if arch is not None else None
+    return int(load_library().fa_check_fp8_args(q, k, v, o, lse, B, H, N, D, scale, q_descale, k_descale,
+                                                v_descale, causal, workspace, workspace_bytes, a))
 
 
 def _dtype_code(t) -> int:
@@ -340,6 +372,35 @@ def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False,
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fwd_fp8(q, k, v, scale: float | None = None, causal: bool = False, q_descale: float = 1.0,
+            k_descale: float = 1.0, v_descale: float = 1.0, stream=None):
+    """FP8 forward (fa_fwd_fp8): q, k, v are uint8 CUDA tensors [B, H, N, D] of E4M3
+    codes; returns (O bf16 [B, H, N, D], lse float32 [B, H, N])."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, D] with the same shape")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.uint8:
+            raise TypeError("%s must hold E4M3 codes as uint8" % name)
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % name)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = fa_fwd_fp8_workspace_bytes(B, H, N, D)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, D,
+                        float(scale), float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+                        ws.data_ptr(), ws.numel(), handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return o, lse
 
 
 def lse_merge(part_o, part_lse, out_dtype=None, out=None, lse=None, stream=None):

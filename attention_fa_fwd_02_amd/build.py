@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
-           os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_bwd.hip")]
+           os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_fp8.hip")]
 HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(CSRC, "fa_device.h"),
            os.path.join(ROOT, "include", "fa.h")]
 

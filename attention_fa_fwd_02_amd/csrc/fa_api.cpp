@@ -301,6 +301,86 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+uint64_t fa_fwd_fp8_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
+    if (B < 1 || H < 1 || N < 1 || D < 1)
+        return 0;
+    const uint64_t npad = ((uint64_t)N + 127u) / 128u * 128u;
+    uint64_t x = 0;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &x) || !mul_ok(x, (uint64_t)D, &x) || !mul_ok(x, npad, &x))
+        return 0;
+    return x;
+}
+
+fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                            int64_t B, int64_t H, int64_t N, int64_t D, float scale, float q_descale,
+                            float k_descale, float v_descale, int causal, const void *workspace,
+                            uint64_t workspace_bytes, const char *arch) {
+    if (!q || !k || !v || !o || !lse || !workspace)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || D < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !std::isfinite(q_descale) || !std::isfinite(k_descale) ||
+        !std::isfinite(v_descale) || !std::isfinite(scale * q_descale * k_descale) ||
+        (causal != 0 && causal != 1))
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace) & 15u)
+        return FA_ERR_INVALID_ARG;
+    if ((uintptr_t)lse & 3u)
+        return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128)
+        return FA_ERR_UNSUPPORTED;
+    // V^T rows are addressed with 32-bit offsets: D * Npad < 2^32
+    if (N >= (int64_t(1) << 24) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
+        return FA_ERR_UNSUPPORTED;
+    const int64_t BH = B * H;
+    if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
+        return FA_ERR_UNSUPPORTED;
+    if (BH * ((N + 255) / 256) >= (int64_t(1) << 23) || BH >= (int64_t(1) << 16))
+        return FA_ERR_UNSUPPORTED;
+    const uint64_t need = fa_fwd_fp8_workspace_bytes(B, H, N, D);
+    if (workspace_bytes < need)
+        return FA_ERR_INVALID_ARG;
+    const uint64_t ib = (uint64_t)(BH * N * D);  // E4M3 inputs
+    const uint64_t ob = ib * 2u;                 // bf16 output
+    const uint64_t lb = (uint64_t)(BH * N) * 4u;
+    const void *ins[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(o, ob, ins[i], ib) || overlaps(lse, lb, ins[i], ib) || overlaps(workspace, need, ins[i], ib))
+            return FA_ERR_INVALID_ARG;
+    if (overlaps(o, ob, lse, lb) || overlaps(o, ob, workspace, need) || overlaps(lse, lb, workspace, need))
+        return FA_ERR_INVALID_ARG;
+    if (arch && std::strncmp(arch, "gfx950", 6) != 0)
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                     int64_t N, int64_t D, float scale, float q_descale, float k_descale, float v_descale,
+                     int causal, void *workspace, uint64_t workspace_bytes, fa_stream_t stream) {
+    fa_status st = fa_check_fp8_args(q, k, v, o, lse, B, H, N, D, scale, q_descale, k_descale, v_descale, causal,
+                                     workspace, workspace_bytes, nullptr);
+    if (st != FA_OK)
+        return st;
+    if ((st = check_device()) != FA_OK)
+        return st;
+    fa::Fp8Args args{};
+    args.q = q;
+    args.k = k;
+    args.v = v;
+    args.vt = workspace;
+    args.o = o;
+    args.lse = lse;
+    args.N = (int32_t)N;
+    args.Npad = (int32_t)((N + 127) / 128 * 128);
+    args.n_qblk = (int32_t)((N + 255) / 256);
+    const float s = scale * q_descale * k_descale;
+    args.c = std::fmax(std::fabs(s) * 1.44269504088896340736f, 1e-30f);
+    args.v_descale = v_descale;
+    args.qneg = std::signbit(s) ? 0x80808080u : 0u;
+    const hipError_t err = fa::launch_fp8((int)D, causal != 0, B * H, args, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
     if (B < 1 || H < 1 || N < 1 || D < 1)
         return 0;

@@ -70,6 +70,41 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)s[0]) + __builtin_bit_cast(float, (uint32_t)s[1]);
 }
 
+struct Work {
+    int bh;
+    int qb;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8), and within
+// an XCD in increasing id.  When the grid is a multiple of 8, XCD x takes the
+// contiguous logical range [x * n/8, (x+1) * n/8), so the query blocks of a
+// slice share one L2.  Causal query blocks differ in length (block qb has
+// qb + 1 blocks' worth of keys): when each XCD's range holds whole slices,
+// they are handed out longest first across the XCD's slices, so the short
+// ones fill in at the end instead of a long one starting last.
+__device__ __forceinline__ Work map_workgroup(int wg, int nwg, int n_qblk, bool causal) {
+    Work w;
+    if ((nwg & 7) == 0) {
+        const int per = nwg >> 3;
+        const int x = wg & 7, j = wg >> 3;
+        if (causal && per % n_qblk == 0) {
+            const int hx = per / n_qblk; // slices per XCD
+            w.bh = x * hx + j % hx;
+            w.qb = n_qblk - 1 - j / hx;
+            return w;
+        }
+        const int L = x * per + j;
+        w.bh = L / n_qblk;
+        const int qb = L - w.bh * n_qblk;
+        w.qb = causal ? (n_qblk - 1 - qb) : qb;
+        return w;
+    }
+    w.bh = wg / n_qblk;
+    const int qb = wg - w.bh * n_qblk;
+    w.qb = causal ? (n_qblk - 1 - qb) : qb; // causal: most key tiles first
+    return w;
+}
+
 // ----------------------------------------------------------------------------
 // 16-bit element types
 // ----------------------------------------------------------------------------

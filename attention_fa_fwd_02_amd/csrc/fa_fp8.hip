@@ -1,0 +1,365 @@
+// FP8 (OCP E4M3) attention forward pass for gfx950.
+//
+// The same tiled online-softmax forward pass as the 16-bit kernels, with
+// both contractions on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands,
+// fp32 accumulation, unit block scales): S^T = K Q^T over the head dim and
+// O^T += V^T P~^T over the keys, with P~ rounded to E4M3.  Per-tensor
+// descale factors multiply the stored values: the scores use
+// c = |scale * q_descale * k_descale| * log2(e) in the one FMA before exp2,
+// and v_descale joins the final 1/l.  FP8 Tensor Core paths are the FA-3
+// direction the pages name (lesson 13 "GPU 内核与 FlashAttention",
+// hpc.payai.win, Q3 answer; "08 · FlashAttention", part 5).
+//
+// Operand layouts (32x32x64: a lane holds 32 consecutive k-values, k = 32 g
+// + 0..31 for lane half g; verified on the device):
+//   S^T: A = K rows, B = Q rows (registers).  The K tile sits in LDS in MFMA
+//        row order: LDS row R of a 32-key block holds key 16 ((R/4)%2) +
+//        4 (R/8) + R%4, so accumulator entry e of lane half g is key 16 g + e.
+//   O^T: A = V^T rows (feature-major), B = P~: for a 64-key step, lane half g
+//        holds its 16 keys of each of the two 32-key blocks, i.e. keys
+//        16 g + 0..15 and 32 + 16 g + 0..15, which are two 16-byte runs of a
+//        V^T row.  V^T comes from fa_fp8_vt_kernel, which transposes V once
+//        per call into the caller's workspace (keys padded with zeros to a
+//        whole key tile).
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kF8Waves = 8;
+constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kF8Rows = 32 * kF8Waves; // query rows per workgroup
+constexpr int kF8BC = 128;              // keys per tile
+constexpr int kScaleOne = 127;          // E8M0 block scale 2^0
+
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, kScaleOne);
+}
+
+// Direct global -> LDS load of 16 bytes per lane with a scalar offset added.
+__device__ __forceinline__ void load_lds_16s(const void *base, uint32_t bytes, uint32_t voff, uint32_t soff,
+                                             lds_char *lds) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Key of LDS row R of a 32-row K block (MFMA row order, see above).
+__device__ __forceinline__ int k_row_key(int R) {
+    return 16 * ((R >> 2) & 1) + 4 * (R >> 3) + (R & 3);
+}
+
+// ----------------------------------------------------------------------------
+// V [BH][N][D] -> V^T [BH][D][Npad], keys N .. Npad-1 zero
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fa_fp8_vt_kernel(const uint8_t *__restrict__ V, uint8_t *__restrict__ Vt,
+                                                        int N, int Npad) {
+    constexpr int TK = 64;              // keys per block
+    constexpr int CH = TK * D / 16;     // 16-byte chunks of the tile (both ways)
+    __shared__ uint8_t tile[TK][D + 4];
+    const int bh = blockIdx.y;
+    const int k0 = blockIdx.x * TK;
+    const uint8_t *src = V + (int64_t)bh * N * D;
+    uint8_t *dst = Vt + (int64_t)bh * D * Npad;
+    for (int ch = threadIdx.x; ch < CH; ch += 256) {
+        const int key = ch / (D / 16), c = ch % (D / 16);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k0 + key < N)
+            v = *(const u32x4 *)(src + (int64_t)(k0 + key) * D + 16 * c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            *(uint32_t *)&tile[key][16 * c + 4 * w] = v[w];
+        }
+    }
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < CH; ch += 256) {
+        const int f = ch / (TK / 16), c = ch % (TK / 16); // feature row, 16-key chunk
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t x = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                x |= (uint32_t)tile[16 * c + 4 * w + b][f] << (8 * b);
+            v[w] = x;
+        }
+        *(u32x4 *)(dst + (int64_t)f * Npad + k0 + 16 * c) = v;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// forward kernel
+// ----------------------------------------------------------------------------
+template <int D>
+struct F8Cfg {
+    static constexpr int KP = D + 16;        // K row pitch (bytes)
+    static constexpr int VTP = kF8BC + 16;   // V^T row pitch (bytes)
+    static constexpr int NK = kF8BC * KP / 1024;
+    static constexpr int NV = D * VTP / 1024;
+    static_assert(NK * 1024 == kF8BC * KP && NV * 1024 == D * VTP, "tiles are whole 1 KB blocks");
+    static constexpr int LPW = (NK + NV + kF8Waves - 1) / kF8Waves;
+    static constexpr int KST = kF8BC * KP;
+    static constexpr int STAGE = 1024 * kF8Waves * LPW;
+    static constexpr int OP = 2 * D + 16;    // bf16 O staging pitch
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
+    using Cfg = F8Cfg<D>;
+    constexpr int BC = kF8BC, KB = BC / 32, DS = D / 64, OB = D / 32;
+    constexpr int KP = Cfg::KP, VTP = Cfg::VTP, OP = Cfg::OP;
+    constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
+    constexpr float kLimit = 256.0f; // P~ <= 2^8: within E4M3's range (448)
+    __shared__ __attribute__((aligned(16))) char stage0_raw[Cfg::STAGE];
+    __shared__ __attribute__((aligned(16))) char stage1_raw[Cfg::STAGE];
+    lds_char *const stage0 = (lds_char *)stage0_raw;
+    lds_char *const stage1 = (lds_char *)stage1_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31;
+    const int g = lane >> 5;
+    const int N = a.N, Npad = a.Npad;
+
+    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    const uint8_t *__restrict__ Q = (const uint8_t *)a.q + (int64_t)wk.bh * N * D;
+    const uint8_t *__restrict__ K = (const uint8_t *)a.k + (int64_t)wk.bh * N * D;
+    const uint8_t *__restrict__ Vt = (const uint8_t *)a.vt + (int64_t)wk.bh * D * Npad;
+    uint16_t *__restrict__ O = (uint16_t *)a.o + (int64_t)wk.bh * N * D;
+    float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
+
+    const int q0 = wk.qb * kF8Rows;
+    const int q0w = q0 + 32 * wave;
+    const int qi = q0w + r;
+    const int kv_end = CAUSAL ? min(N, q0 + kF8Rows) : N;
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    // loader: load j of wave w fills 1 KB block w + 8 j of the stage; blocks
+    // [0, NK) hold the K tile (rows in MFMA row order), [NK, NK + NV) the V^T
+    // tile (feature rows, 128 keys each), the rest are spare
+    uint32_t voff[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int blk = wave + kF8Waves * j;
+        uint32_t off = 0;
+        if (blk < NK) {
+            const int pos = 1024 * blk + 16 * lane;
+            const int R = pos / KP, chunk = (pos % KP) / 16;
+            const int key = 32 * (R >> 5) + k_row_key(R & 31);
+            off = (uint32_t)(key * D + (chunk < D / 16 ? 16 * chunk : 0));
+        } else if (blk < NK + NV) {
+            const int pos = 1024 * (blk - NK) + 16 * lane;
+            const int f = pos / VTP, chunk = (pos % VTP) / 16;
+            off = (uint32_t)f * (uint32_t)Npad + (chunk < BC / 16 ? 16u * chunk : 0u);
+        }
+        voff[j] = off;
+    }
+    const uint32_t vt_bytes = __builtin_amdgcn_readfirstlane((uint32_t)D * (uint32_t)Npad);
+    auto issue_tile = [&](int t, lds_char *st) {
+        const int k0 = t * BC;
+        const uint32_t k_bytes =
+            __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D));
+        // V^T rows hold keys up to Npad (zero-padded); a tile past the last loads nothing
+        const uint32_t v_bytes = k0 < kv_end ? vt_bytes : 0u;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int blk = wave + kF8Waves * j; // wave-uniform
+            lds_char *dst = st + 1024 * blk;
+            if (blk >= NK && blk < NK + NV)
+                load_lds_16s(Vt, v_bytes, voff[j], (uint32_t)k0, dst);
+            else
+                load_lds_16s(K + (int64_t)k0 * D, k_bytes, voff[j], 0u, dst);
+        }
+    };
+
+    // B operand of S^T: lane (r, g) holds q_qi[64 s + 32 g .. + 31]; a negative
+    // scale flips the sign bit of every E4M3 byte
+    i32x8 qf[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+        if (qi < N) {
+            const u32x4 lo = *(const u32x4 *)(Q + (int64_t)qi * D + 64 * s + 32 * g);
+            const u32x4 hi = *(const u32x4 *)(Q + (int64_t)qi * D + 64 * s + 32 * g + 16);
+            qf[s] = i32x8{(int)(lo[0] ^ a.qneg), (int)(lo[1] ^ a.qneg), (int)(lo[2] ^ a.qneg), (int)(lo[3] ^ a.qneg),
+                          (int)(hi[0] ^ a.qneg), (int)(hi[1] ^ a.qneg), (int)(hi[2] ^ a.qneg), (int)(hi[3] ^ a.qneg)};
+        } else {
+            qf[s] = i32x8{};
+        }
+    }
+
+    f32x16 o[OB];
+#pragma unroll
+    for (int b = 0; b < OB; ++b)
+        o[b] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const float c = a.c;
+    const int k_lane = r * KP + 32 * g;      // LDS row r of a K block, k half g
+    const int v_lane = r * VTP + 16 * g;     // V^T row r of a feature block
+
+    auto tile = [&](int t, const lds_char *cur, lds_char *next) {
+        const int k0 = t * BC;
+        const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
+        if (active) {
+            f32x16 s[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                s[kb] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < DS; ++st)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const lds_char *p = cur + k_lane + 32 * kb * KP + 64 * st;
+                    const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
+                    const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 16);
+                    const i32x8 kv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    s[kb] = mfma8(kv, qf[st], s[kb]);
+                }
+            issue_tile(t + 1, next);
+            // entry e of block kb, lane half g: key k0 + 32 kb + 16 g + e
+            if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
+                const int lim = (CAUSAL ? min(N, qi + 1) : N) - k0 - 16 * g;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        s[kb][e] = (32 * kb + e < lim) ? s[kb][e] : -INFINITY;
+            }
+            // P~ = exp2(s c - m_ref) <= 2^8, summed in fp32, rounded to E4M3 for PV:
+            // pk[kb][w] holds entries 4w .. 4w+3 of block kb
+            uint32_t pk[KB][4];
+            float lt = 0.f;
+            auto exps = [&](float m_ref) {
+                lt = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        float p[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + u], c, -m_ref));
+                            lt += p[u];
+                        }
+                        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                        x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
+                        pk[kb][w] = (uint32_t)x;
+                    }
+            };
+            bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+            if (!move) {
+                exps(m_run);
+                move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
+            }
+            if (move) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        mx = fmaxf(mx, s[kb][e]);
+                const float m_new = fmaxf(m_run, pair_max(mx) * c);
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int b = 0; b < OB; ++b)
+                    o[b] *= alpha;
+                m_run = m_new;
+                exps(m_run == -INFINITY ? 0.f : m_run);
+            }
+            l_run += lt;
+            // O^T += V^T P~^T over 64-key steps (blocks 2 s', 2 s' + 1)
+            const lds_char *vs = cur + Cfg::KST + v_lane;
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int sp = 0; sp < KB / 2; ++sp) {
+                    const lds_char *p = vs + 32 * b * VTP + 64 * sp;
+                    const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
+                    const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 32);
+                    const i32x8 vv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    const i32x8 pb = {(int)pk[2 * sp][0], (int)pk[2 * sp][1], (int)pk[2 * sp][2], (int)pk[2 * sp][3],
+                                      (int)pk[2 * sp + 1][0], (int)pk[2 * sp + 1][1], (int)pk[2 * sp + 1][2],
+                                      (int)pk[2 * sp + 1][3]};
+                    o[b] = mfma8(vv, pb, o[b]);
+                }
+        } else {
+            issue_tile(t + 1, next);
+        }
+        wait_vmcnt<0>();
+        tile_barrier();
+    };
+
+    issue_tile(0, stage0);
+    wait_vmcnt<0>();
+    tile_barrier();
+    int t = 0;
+    for (; t + 2 <= n_tiles; t += 2) {
+        tile(t, stage0, stage1);
+        tile(t + 1, stage1, stage0);
+    }
+    if (t < n_tiles)
+        tile(t, stage0, stage1);
+
+    // epilogue: O = acc * v_descale / l in bf16, staged through LDS; lse
+    const float l_tot = pair_sum(l_run);
+    const float inv = a.v_descale / l_tot;
+    static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
+    tile_barrier();
+    lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
+    if (q0w < N) {
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const u32x2 w = {Bf16::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
+                                 Bf16::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
+                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
+            }
+        if (g == 0 && qi < N)
+            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    __syncthreads();
+    if (q0w < N) {
+#pragma unroll
+        for (int j = 0; j < 32 * (D / 8) / 64; ++j) {
+            const int ch = 64 * j + lane;
+            const int row = ch / (D / 8), col = ch % (D / 8);
+            const int q = q0w + row;
+            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
+            if (q < N)
+                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_fp8_t(bool causal, int64_t BH, const Fp8Args &args, hipStream_t stream) {
+    const dim3 tgrid((unsigned)(args.Npad / 64), (unsigned)BH);
+    hipLaunchKernelGGL((fa_fp8_vt_kernel<D>), tgrid, dim3(256), 0, stream, (const uint8_t *)args.v,
+                       (uint8_t *)args.vt, args.N, args.Npad);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t nwg = BH * (int64_t)args.n_qblk;
+    if (causal)
+        hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, true>), dim3((unsigned)nwg), dim3(kF8Threads), 0, stream, args);
+    else
+        hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, false>), dim3((unsigned)nwg), dim3(kF8Threads), 0, stream, args);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_fp8(int D, bool causal, int64_t BH, const Fp8Args &args, hipStream_t stream) {
+    return D == 64 ? launch_fp8_t<64>(causal, BH, args, stream) : launch_fp8_t<128>(causal, BH, args, stream);
+}
+
+} // namespace fa

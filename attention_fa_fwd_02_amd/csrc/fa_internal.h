@@ -51,6 +51,24 @@ constexpr int query_block(int64_t D) { return D > 192 ? 128 : 256; }
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
                       const FwdArgs &args, hipStream_t stream);
 
+// FP8 (E4M3) forward arguments, passed by value.
+struct Fp8Args {
+    const void *q;      // [B*H][N][D] E4M3
+    const void *k;
+    const void *v;
+    void *vt;           // workspace: V^T [B*H][D][Npad] E4M3, keys >= N zero
+    void *o;            // [B*H][N][D] bf16
+    float *lse;         // [B*H][N]
+    int32_t N;
+    int32_t Npad;       // N rounded up to the 128-key tile
+    int32_t n_qblk;     // ceil(N / 256)
+    float c;            // |scale * q_descale * k_descale| * log2(e)
+    float v_descale;
+    uint32_t qneg;      // 0x80808080 when scale * q_descale * k_descale < 0
+};
+
+hipError_t launch_fp8(int D, bool causal, int64_t BH, const Fp8Args &args, hipStream_t stream);
+
 // Backward-pass kernel arguments, passed by value.
 struct BwdArgs {
     const void *q;

@@ -22,7 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, B4 H16 N4096 D128"
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}  # MI355X dense MFMA, published
 # the forward kernel's sources: the kernel file and the device helpers it includes
 KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_mfma_bf16_d128_B4H16N4096_counters.txt")
@@ -307,6 +307,46 @@ def bench_bwd(name, steps, warmup):
         % (name, B, H, N, D, causal, ms, tf, 100 * tf / PEAK_TFLOPS["bf16"]))
 
 
+def bench_fp8(name, steps, warmup):
+    """fa_fwd_fp8 on the headline shape (B4 H16 N4096 D128, E4M3 inputs, bf16 O;
+    stderr line only).  FLOPs as for the 16-bit path; peak: dense FP8 MFMA."""
+    import numpy as np
+    import torch
+
+    import attention_fa_fwd_02_amd as fa
+    import fa_inputs as fi
+    causal = name.endswith("causal")
+    B, H, N, D = 4, 16, 4096, 128
+    q, k, v = fi.make_qkv(B, H, N, D, "e4m3", 1004)
+    dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (q, k, v))
+    o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    wsb = fa.fa_fwd_fp8_workspace_bytes(B, H, N, D)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(D)
+
+    def step():
+        st = fa.fa_fwd_fp8(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, D,
+                           scale, 1.0, 1.0, 1.0, int(causal), ws.data_ptr(), wsb, stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_fwd_fp8")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    tf = fi.workload_flops(B, H, N, D, causal) / (ms * 1e-3) / 1e12
+    log("%s: B%d H%d N%d D%d e4m3 causal=%d  step %.4f ms (V transpose included)  %.1f TFLOP/s  %.1f%% of fp8 peak"
+        % (name, B, H, N, D, causal, ms, tf, 100 * tf / PEAK_TFLOPS["e4m3"]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +379,8 @@ def main():
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("bwd", "bwd_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
+        for name in ("fp8", "fp8_causal"):
+            bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     r = main_res
     if not args.no_cpu_baseline:
         r["cpu_baseline"] = cpu_baseline(*main_ctx)

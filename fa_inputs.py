@@ -10,13 +10,15 @@ Recipe (stated once, used everywhere):
     ``SeedSequence(seed).spawn(3)`` in that order;
   * each element is ``standard_normal(dtype=float32) * sigma``;
   * for bf16 / fp16 storage the fp32 draw is rounded to nearest-even
-    (bf16 kept as its 16-bit pattern, a uint16 array).
+    (bf16 kept as its 16-bit pattern, a uint16 array); for FP8 E4M3 storage
+    it is rounded to the nearest E4M3 value (ties to even, saturating at
+    448), kept as uint8 codes.
 """
 from __future__ import annotations
 
 import numpy as np
 
-DTYPES = ("f32", "bf16", "f16")
+DTYPES = ("f32", "bf16", "f16", "e4m3")
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -32,6 +34,28 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the 127 non-negative finite OCP FP8 E4M3 codes 0x00..0x7E, by code."""
+    codes = np.arange(127)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+    no infinities): nearest value, ties to the even code, magnitudes beyond 448
+    saturate to 448.  Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = _e4m3_magnitudes()
+    a = np.minimum(np.abs(x), mags[-1])
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, len(mags) - 1)
+    lo = hi - 1
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a == mags[hi], hi, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
 
@@ -44,6 +68,8 @@ def _draw(rng: np.random.Generator, shape, sigma: float, dtype: str, chunk: int 
         out = np.empty(n, dtype=np.float16)
     elif dtype == "bf16":
         out = np.empty(n, dtype=np.uint16)
+    elif dtype == "e4m3":
+        out = np.empty(n, dtype=np.uint8)
     else:
         raise ValueError(dtype)
     for s in range(0, n, chunk):
@@ -55,6 +81,8 @@ def _draw(rng: np.random.Generator, shape, sigma: float, dtype: str, chunk: int 
             out[s:e] = x
         elif dtype == "f16":
             out[s:e] = x.astype(np.float16)  # numpy rounds to nearest-even
+        elif dtype == "e4m3":
+            out[s:e] = f32_to_e4m3_bits(x)
         else:
             out[s:e] = f32_to_bf16_bits(x)
     return out.reshape(shape)

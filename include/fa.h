@@ -263,6 +263,58 @@ fa_status fa_check_varlen_args(const void *q, const void *k, const void *v, cons
                                int dtype, const char *arch);
 
 /*
+ * FP8 forward pass.  q, k, v hold OCP FP8 E4M3 values (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; S.1111.111 is NaN), each multiplied by
+ * a per-tensor descale factor: the attention computed is that of
+ * q * q_descale, k * k_descale and v * v_descale.  Both contractions run on
+ * the gfx950 FP8 matrix instructions with fp32 accumulation, the FA-3
+ * direction the pages name (lesson 13 "GPU 内核与 FlashAttention",
+ * hpc.payai.win, Q3 answer): S = (q . k) from E4M3 operands, and O from
+ * P~ (the exp2 weights, each <= 2^8) rounded to E4M3 times E4M3 v.  O is
+ * bf16, lse fp32 as for fa_fwd.  The rounding of P~ to E4M3 (relative error
+ * up to 2^-4 per weight) bounds |O - O_exact| by 2^-4 * sum_j p_ij |v_j| per
+ * element, before the bf16 rounding of O.
+ *
+ * fa_fwd_fp8_workspace_bytes -- device workspace fa_fwd_fp8 needs:
+ * B*H*D*Npad bytes with Npad = N rounded up to 128 (V transposed per call).
+ * Returns 0 if an argument is < 1 or the size overflows.  Host only.
+ */
+uint64_t fa_fwd_fp8_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+
+/*
+ * fa_fwd_fp8 -- enqueue the FP8 forward pass on `stream` (two kernels: V
+ * transposed into the workspace, then attention).
+ *
+ *   q, k, v     device pointers, [B, H, N, D] of E4M3 bytes, 16-byte aligned.
+ *   o           device pointer, [B, H, N, D] bf16, overwritten.
+ *   lse         device pointer, [B, H, N] fp32, overwritten (natural-log
+ *               logsumexp of scale * (q q_descale) . (k k_descale)).
+ *   B, H, N     >= 1, N < 2^24.
+ *   D           64 or 128.
+ *   scale, q_descale, k_descale, v_descale  finite floats.
+ *   causal      0 or 1 (key j visible to query i iff j <= i).
+ *   workspace   device pointer, 16-byte aligned, at least
+ *               fa_fwd_fp8_workspace_bytes bytes; overwritten.
+ *
+ * Errors: FA_ERR_INVALID_ARG for a NULL pointer, B/H/N/D < 1, a non-finite
+ * scale or descale, causal not 0/1, misalignment, a workspace too small, or
+ * outputs / workspace overlapping each other or an input; FA_ERR_UNSUPPORTED
+ * for D other than 64/128, N >= 2^24, B*H >= 2^16, the size limits of
+ * fa_fwd, or a device that is not gfx950; FA_ERR_HIP when a device query or
+ * a launch fails.  All checks precede any HIP call; the library allocates
+ * nothing.
+ */
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                     int64_t N, int64_t D, float scale, float q_descale, float k_descale, float v_descale,
+                     int causal, void *workspace, uint64_t workspace_bytes, fa_stream_t stream);
+
+/* fa_check_fp8_args -- the argument checks of fa_fwd_fp8 on the host only. */
+fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                            int64_t B, int64_t H, int64_t N, int64_t D, float scale, float q_descale,
+                            float k_descale, float v_descale, int causal, const void *workspace,
+                            uint64_t workspace_bytes, const char *arch);
+
+/*
  * Backward pass.  The forward pass keeps only O and lse; the backward pass
  * recomputes P = exp(scale * q.k - lse) tile by tile on chip rather than
  * reading a stored N x N matrix ("08 · FlashAttention", part 3, on the

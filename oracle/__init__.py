@@ -91,10 +91,19 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     dtype 'f32' / 'f16': the array holds those floats.
     dtype 'bf16': the array holds the 16-bit patterns (uint16); a bf16 value
     is the fp32 value whose upper 16 bits are the pattern.
+    dtype 'e4m3': the array holds OCP FP8 E4M3 codes (uint8).
     """
     if dtype == "bf16":
         bits = np.ascontiguousarray(x).view(np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        # OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+        # field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities
+        b = np.ascontiguousarray(x).view(np.uint8).astype(np.int64)
+        e, m = (b >> 3) & 15, b & 7
+        mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+        return np.where(b & 0x80, -mag, mag)
     if dtype == "f16":
         return np.asarray(x, dtype=np.float16).astype(np.float64)
     if dtype == "f32":

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libfa
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"fa_fwd", "fa_check_args", "fa_status_string", "fa_abi_version",
                           "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
                           "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args", "fa_bwd",
-                          "fa_bwd_workspace_bytes", "fa_check_bwd_args"}
+                          "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
+                          "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -329,3 +330,42 @@ def test_bwd_reports_invalid_args_before_any_hip_call():
     assert st == fa.FA_ERR_INVALID_ARG
     st = fa.fa_bwd(BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 128, 0.1, 1, 0, BWS, 12000, 0)
     assert st == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ FP8
+
+F8 = dict(q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T, B=2, H=3, N=1000, D=128, scale=0.1, qd=0.5, kd=2.0, vd=1.5,
+          causal=0, ws=6 * T, wsb=2 * 3 * 128 * 1024)
+
+
+def f8check(arch="gfx950", **kw):
+    a = dict(F8)
+    a.update(kw)
+    return fa.fa_check_fp8_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"],
+                                a["scale"], a["qd"], a["kd"], a["vd"], a["causal"], a["ws"], a["wsb"], arch)
+
+
+def test_fp8_workspace_bytes():
+    assert fa.fa_fwd_fp8_workspace_bytes(2, 3, 1000, 128) == 2 * 3 * 128 * 1024
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 1, 128, 64) == 64 * 128
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 0, 128, 64) == 0
+
+
+def test_fp8_good_arguments_pass():
+    assert f8check() == fa.FA_OK and f8check(arch=None) == fa.FA_OK
+    assert f8check(D=64, causal=1, scale=-0.3, qd=-1.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(lse=0), dict(ws=0), dict(N=0), dict(scale=float("inf")), dict(qd=float("nan")),
+    dict(vd=float("inf")), dict(scale=1e30, qd=1e30), dict(causal=2), dict(q=T + 4), dict(o=4 * T + 2),
+    dict(lse=5 * T + 1), dict(ws=6 * T + 8), dict(wsb=2 * 3 * 128 * 1024 - 1), dict(o=T + 64),
+    dict(ws=3 * T - 64), dict(lse=4 * T + 128),
+])
+def test_fp8_invalid_arguments(kw):
+    assert f8check(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(N=1 << 24), dict(B=1 << 8, H=1 << 8)])
+def test_fp8_unsupported(kw):
+    assert f8check(**kw, wsb=1 << 62) == fa.FA_ERR_UNSUPPORTED

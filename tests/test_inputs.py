@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import fa_inputs as fi
+import oracle
 
 
 def test_bf16_rounding_matches_torch_rne():
@@ -50,3 +51,24 @@ def test_workload_table():
     assert (w["B"], w["H"], w["N"], w["D"], w["dtype"]) == (4, 16, 4096, 128, "bf16")
     assert fi.workload_flops(4, 16, 4096, 128, False) == 549755813888.0
     assert fi.workload_flops(4, 16, 4096, 128, True) == 549755813888.0 / 2
+
+
+def test_e4m3_decode_fixed_points():
+    """OCP FP8 E4M3 code points: 1.0 = 0 0111 000, the largest normal 448 =
+    0 1111 110, the smallest normal 2^-6 = 0 0001 000, the smallest subnormal
+    2^-9 = 0 0000 001, NaN = S 1111 111, and the sign bit."""
+    codes = np.array([0x38, 0x7E, 0x08, 0x01, 0x00, 0xB8, 0x40, 0x3C, 0x07], dtype=np.uint8)
+    want = np.array([1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 0.0, -1.0, 2.0, 1.5, 7 * 2.0 ** -9])
+    assert np.array_equal(oracle.widen(codes, "e4m3"), want)
+    assert np.isnan(oracle.widen(np.array([0x7F, 0xFF], dtype=np.uint8), "e4m3")).all()
+
+
+def test_e4m3_round_trip_and_rounding():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.widen(codes, "e4m3")
+    assert np.array_equal(fi.f32_to_e4m3_bits(vals), codes)
+    # midpoints round to the even code; beyond 448 saturates
+    mid = (vals[(codes >= 0x08) & (codes < 0x7E)] + oracle.widen(codes[(codes >= 0x08) & (codes < 0x7E)] + 1, "e4m3")) / 2
+    got = fi.f32_to_e4m3_bits(mid)
+    assert np.all(got % 2 == 0)
+    assert list(fi.f32_to_e4m3_bits(np.array([449.0, 1e6, -1e6]))) == [0x7E, 0x7E, 0xFE]
