@@ -8,7 +8,7 @@
 // c = |scale * q_descale * k_descale| * log2(e) in the one FMA before exp2,
 // and v_descale joins the final 1/l.  FP8 Tensor Core paths are the FA-3
 // direction the pages name (lesson 13 "GPU 内核与 FlashAttention",
-// hpc.payai.win, Q3 answer; "08 · FlashAttention", part 5).
+// hpc.payai.win, answer to Q3).
 //
 // Operand layouts (32x32x64: a lane holds 32 consecutive k-values, k = 32 g
 // + 0..31 for lane half g; verified on the device):
