@@ -50,11 +50,14 @@
 // address an affine function of lane and loop index (immediate offsets, no
 // per-read VALU work).
 //
-// Pipelining: the next K/V tile is fetched from HBM/L2 into registers while
-// the current tile is computed, then written to the other LDS buffer
-// (double buffering, pwwt.cn essay section 3.3), one barrier per tile.  O is
-// staged through LDS at the end so each row is stored as full 16-byte
-// chunks covering whole cache lines.
+// Pipelining: the next K/V tile goes from HBM/L2 straight into the other LDS
+// buffer (direct-to-LDS buffer loads) while the current tile is computed
+// (double buffering, pwwt.cn essay section 3.3), one barrier per tile.  For
+// [B, H, N, D] slices with 128-key tiles (D <= 128) fa_fwd_pp_kernel runs the
+// same tile work in a ping-pong order instead: the two waves of a SIMD run
+// half a tile apart, so one issues MFMAs while the other computes
+// exponentials.  O is staged through LDS at the end so each row is stored as
+// full 16-byte chunks covering whole cache lines.
 //
 // fp32 path (v_mfma_f32_32x32x2_f32): same decomposition; one element per
 // lane per MFMA, so V needs no transpose; K rows are padded by one word;
@@ -152,6 +155,8 @@ struct MfmaCfg {
     static constexpr int STAGES = 2;
     static constexpr int LDS = STAGES * STAGE;
     static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
+    // two wave groups per SIMD and 128-key tiles: the ping-pong schedule
+    static constexpr bool PINGPONG = WAVES == 8 && BC == 128;
 };
 
 template <typename E, int D, bool CAUSAL, int MODE>
@@ -534,6 +539,325 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 }
 
 // ----------------------------------------------------------------------------
+// bf16 / fp16 MFMA kernel, ping-pong schedule ([B, H, N, D] slices, head dims
+// with 128-key tiles)
+// ----------------------------------------------------------------------------
+// Same tiles, operand layouts, masking and online softmax as
+// fa_fwd_mfma_kernel; only the order of work differs.  A wave's work on key
+// tile t splits into
+//   M(t): O += P(t-1) V(t-1), then S(t) = K(t) Q^T   (MFMA, LDS reads)
+//   X(t): mask and online softmax of S(t) into P(t)   (VALU)
+// and every wave runs M(0) X(0) M(1) X(1) ... M(T), one item per phase, with
+// a workgroup barrier after every phase.  Waves 4..7 run one phase behind
+// waves 0..3; waves w and w + 4 share a SIMD, so in every phase one of them
+// issues MFMAs while the other does its exponentials, and the matrix core is
+// not left idle while both do softmax work, as happens when the two waves of
+// a SIMD step through the same tile in lockstep.
+//
+// V tiles trail K tiles by one: batch b brings the K rows of tile b and the
+// V rows of tile b - 1.  Batch c + 1 is issued at the start of phase 2c and
+// waited for at the end of phase 2c + 1; K(t) is read in phases 2t and
+// 2t + 1 and V(t) in phases 2t + 2 and 2t + 3, so two K stages and two V
+// stages (separate LDS objects, so the loads into one are never waited for
+// before reads of another) hold every tile for as long as it is read.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs a) {
+    using Cfg = MfmaCfg<D>;
+    static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
+    constexpr int W = Cfg::WAVES, QBLK = Cfg::QBLK, BC = Cfg::BC;
+    constexpr int KB = BC / 32, DC = D / 16, OB = D / 32, KCH = D / 8;
+    constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
+    constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
+    constexpr int KBYTES = NK * 1024;               // K stage: the K tile
+    constexpr int VBYTES = (W * LPW - NK) * 1024;   // V stage: the V tile and the spare blocks
+    static_assert(NV * 1024 <= VBYTES && KBYTES <= VBYTES, "stage sizes");
+    constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8: deferred-rescale threshold
+    __shared__ __attribute__((aligned(16))) char ks0_raw[KBYTES];
+    __shared__ __attribute__((aligned(16))) char ks1_raw[KBYTES];
+    __shared__ __attribute__((aligned(16))) char vs0_raw[VBYTES];
+    __shared__ __attribute__((aligned(16))) char vs1_raw[VBYTES];
+    lds_char *const ks0 = (lds_char *)ks0_raw;
+    lds_char *const ks1 = (lds_char *)ks1_raw;
+    lds_char *const vs0 = (lds_char *)vs0_raw;
+    lds_char *const vs1 = (lds_char *)vs1_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2; // waves w and w + 4 share a SIMD and sit in different groups
+    const int r = lane & 31;
+    const int g = lane >> 5;
+
+    // --- slice and query block ---------------------------------------------
+    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    const int N = a.N;
+    const int64_t off = (int64_t)wk.bh * N * D;
+    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + off;
+    const uint16_t *__restrict__ K = (const uint16_t *)a.k + off;
+    const uint16_t *__restrict__ V = (const uint16_t *)a.v + off;
+    uint16_t *__restrict__ O = (uint16_t *)a.o + off;
+    float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
+    const int q0 = wk.qb * QBLK;
+    const int q0w = q0 + 32 * wave; // first query row of this wave
+    const int qi = q0w + r;         // this lane's query row
+    // keys [0, kv_end): all of them, or up to the block's last query when causal
+    const int kv_end = CAUSAL ? min(N, q0 + QBLK) : N;
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    // --- loader: batch b = the K rows of tile b and the V rows of tile b - 1 --
+    // Load j of wave w fills 1 KB block w + 8j: blocks below NK go to the K
+    // stage, the rest to the V stage (the V tile, then spare blocks that
+    // re-read the tile's first row).  Descriptors stop at kv_end: rows past it
+    // read as zeros.
+    static_assert(BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
+    uint32_t voff2[(LPW + 1) / 2];
+#pragma unroll
+    for (int j = 0; j < (LPW + 1) / 2; ++j)
+        voff2[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int blk = wave + W * j;
+        const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
+        const int pitch = is_k ? KP : VP;
+        const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
+        const int chunk = (pos % pitch) / 16;
+        const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
+        voff2[j / 2] |= off << (16 * (j % 2));
+    }
+    auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
+        const int kk = b * BC, kv = max(b - 1, 0) * BC;
+        const uint32_t kbytes =
+            __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D * 2 : 0));
+        const uint32_t vbytes = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(b >= 1 && b - 1 < n_tiles ? min(kv_end - kv, BC) * D * 2 : 0));
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int blk = wave + W * j; // wave-uniform
+            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+            if (blk < NK)
+                load_lds_16(K + (int64_t)kk * D, kbytes, off, kd + 1024 * blk);
+            else
+                load_lds_16(V + (int64_t)kv * D, vbytes, off, vd + 1024 * (blk - NK));
+        }
+    };
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const int k_lane = (8 * (r >> 3) + 2 * (r & 3) + ((r >> 2) & 1)) * KP + 16 * g;
+    const int v_lane = (g + 2 * ((lane >> 2) & 3)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+    u32x4 qf[DC];
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) {
+        qf[cc] = qi < N ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
+        qf[cc] ^= a.qneg;
+    }
+    f32x16 o[OB];
+#pragma unroll
+    for (int b = 0; b < OB; ++b)
+        o[b] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const float c = a.c;
+    f32x16 s[KB];       // S^T of the wave's current tile
+    uint32_t pk[KB][8]; // its weights, rounded, as the PV operand
+
+    // a tile is skipped by a wave none of whose rows sees any of its keys
+    auto active = [&](int t) __attribute__((always_inline)) {
+        return (q0w < N) && (!CAUSAL || t * BC <= q0w + 31);
+    };
+    // S^T = K Q^T : s[kb][i] = score(query qi, key k0 + 32kb + 2i + g)
+    auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
+        const lds_char *ks = kst + k_lane;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            s[kb] = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(ks + 32 * kb * KP + 32 * cc);
+                s[kb] = E::mfma(kv, qf[cc], s[kb]);
+            }
+        // four K reads ahead of the MFMAs, then one read per MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int n = 0; n < KB * DC - 4; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // O^T += V^T P^T : o[b][i] accumulates feature 32b + 8(i/4) + 4g + i%4 of
+    // query qi.  Consecutive MFMAs go to different accumulators; each o[b]
+    // still adds its (kb, mm) terms in order.
+    auto accumulate = [&](const lds_char *vst) __attribute__((always_inline)) {
+        const lds_char *vs = vst + v_lane;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int b = 0; b < OB; ++b) {
+                    const lds_char *vp = vs + (32 * kb + 16 * mm) * VP + 64 * b;
+                    const i16x4 lo =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vp);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4 *)(vp + 8 * VP));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                    const u32x4 vv = {l2[0], l2[1], h2[0], h2[1]};
+                    const u32x4 pb = {pk[kb][4 * mm], pk[kb][4 * mm + 1], pk[kb][4 * mm + 2], pk[kb][4 * mm + 3]};
+                    o[b] = E::mfma(vv, pb, o[b]);
+                }
+        // eight transposing reads (four MFMAs) ahead, then two per MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int n = 0; n < OB * KB * 2 - 4; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * BC;
+        // masking: keys beyond N, and keys after the query when causal
+        if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + 32 * kb + 2 * i + g;
+                    const bool vis = key < N && (!CAUSAL || key <= qi);
+                    s[kb][i] = vis ? s[kb][i] : -INFINITY;
+                }
+        }
+        float lt = 0.f;
+        auto exps = [&](float m_ref) __attribute__((always_inline)) {
+            lt = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
+                    lt += p0 + p1;
+                    pk[kb][i >> 1] = E::pack(p0, p1);
+                }
+        };
+        bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+        if (!move) {
+            exps(m_run);
+            move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
+        }
+        if (move) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[kb][i]);
+            const float m_new = fmaxf(m_run, pair_max(mx) * c);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+                o[b] *= alpha;
+            m_run = m_new;
+            exps(m_run == -INFINITY ? 0.f : m_run);
+        }
+        l_run += lt;
+    };
+    auto M = [&](int t, const lds_char *vprev, const lds_char *kcur) __attribute__((always_inline)) {
+        if (t >= 1 && t - 1 < n_tiles && active(t - 1))
+            accumulate(vprev);
+        if (t < n_tiles && active(t))
+            scores(kcur);
+    };
+    auto X = [&](int t) __attribute__((always_inline)) {
+        if (t >= 0 && t < n_tiles && active(t))
+            softmax(t);
+    };
+
+    issue_batch(0, ks0, vs1);
+    wait_vmcnt<0>();
+    tile_barrier();
+    // Phase 2c: batch c + 1 goes out; group 0 runs M(c), group 1 X(c - 1).
+    // Phase 2c + 1: group 0 runs X(c), group 1 M(c); batch c + 1 has landed.
+    // Each group runs a straight-line loop of its own; both pass the same
+    // number of barriers.  Tile c is in stage c % 2.
+    if (grp == 0) {
+        auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
+                        __attribute__((always_inline)) {
+            if (cc + 1 <= n_tiles)
+                issue_batch(cc + 1, kn, vn);
+            M(cc, vprev, kcur);
+            tile_barrier();
+            X(cc);
+            wait_vmcnt<0>();
+            tile_barrier();
+        };
+        int cc = 0;
+        for (; cc + 1 <= n_tiles; cc += 2) {
+            step(cc, ks1, vs0, vs1, ks0);
+            step(cc + 1, ks0, vs1, vs0, ks1);
+        }
+        if (cc <= n_tiles)
+            step(cc, ks1, vs0, vs1, ks0);
+    } else {
+        auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
+                        __attribute__((always_inline)) {
+            if (cc + 1 <= n_tiles)
+                issue_batch(cc + 1, kn, vn);
+            X(cc - 1);
+            tile_barrier();
+            M(cc, vprev, kcur);
+            wait_vmcnt<0>();
+            tile_barrier();
+        };
+        int cc = 0;
+        for (; cc + 1 <= n_tiles; cc += 2) {
+            step(cc, ks1, vs0, vs1, ks0);
+            step(cc + 1, ks0, vs1, vs0, ks1);
+        }
+        if (cc <= n_tiles)
+            step(cc, ks1, vs0, vs1, ks0);
+    }
+
+    // --- epilogue: every tile read is done; O / l is staged through LDS
+    // (waves 2i and 2i + 1 in stage array i, wave-private rows), lse ---------
+    const int sa = wave >> 1;
+    lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
+    const float l_tot = pair_sum(l_run);
+    const float inv = 1.0f / l_tot;
+    static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
+    lds_char *ow = own + (wave & 1) * 32 * OP;
+    if (q0w < N) {
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const u32x2 w = {E::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
+                                 E::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
+                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
+            }
+        if (g == 0 && qi < N)
+            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    __syncthreads();
+    if (q0w < N) {
+        constexpr int kChunks = 32 * KCH;
+#pragma unroll
+        for (int j = 0; j < kChunks / 64; ++j) {
+            const int ch = 64 * j + lane;
+            const int row = ch / KCH, col = ch % KCH;
+            const int q = q0w + row;
+            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
+            if (q < N)
+                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2_f32)
 // ----------------------------------------------------------------------------
 template <int D>
@@ -787,9 +1111,15 @@ template <typename E, int D, int MODE>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     constexpr int T = MfmaCfg<D>::THREADS;
-    if (causal)
-        return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
-    return launch<fa_fwd_mfma_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
+    if constexpr (MODE == kDense && MfmaCfg<D>::PINGPONG) {
+        if (causal)
+            return launch<fa_fwd_pp_kernel<E, D, true>, T>(nwg, 0, args, stream);
+        return launch<fa_fwd_pp_kernel<E, D, false>, T>(nwg, 0, args, stream);
+    } else {
+        if (causal)
+            return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
+        return launch<fa_fwd_mfma_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
+    }
 }
 
 // head dims of the 16-bit kernels

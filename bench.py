@@ -25,7 +25,7 @@ METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, B4 H16 N4096 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}  # MI355X dense MFMA, published
 # the forward kernel's sources: the kernel file and the device helpers it includes
 KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
-COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_mfma_bf16_d128_B4H16N4096_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_pp_bf16_d128_B4H16N4096_counters.txt")
 
 WORKLOADS = {
     # name: (B, H, N, D, dtype, causal, sigma)
@@ -406,7 +406,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["achieved"] / r["peak"], 4),
                      "traffic": traffic,
-                     "kernel": "fa_fwd_mfma_kernel<%s, D=%d, causal=%d>" % (r["dtype"], r["D"], r["causal"]),
+                     "kernel": "fa_fwd_pp_kernel<%s, D=%d, causal=%d>" % (r["dtype"], r["D"], r["causal"]),
                      "kernel_avg_ms": round(r["kernel_ms"], 5)},
         "cpu_baseline": r.get("cpu_baseline"),
     }
