@@ -21,6 +21,13 @@
 //        V^T row.  V^T comes from fa_fp8_vt_kernel, which transposes V once
 //        per call into the caller's workspace (keys padded with zeros to a
 //        whole key tile).
+//
+// Schedule: the ping-pong order of the 16-bit dense kernel.  A wave's tile
+// work is split into an MFMA phase (PV of the previous tile, then the
+// scores of this one) and a softmax phase; waves 4..7 run one phase behind
+// waves 0..3, so the two waves of a SIMD overlap one's MFMAs with the
+// other's exponentials.  V^T tiles trail K tiles by one, in two K and two
+// V^T stages.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -34,6 +41,7 @@ constexpr int kF8Threads = 64 * kF8Waves;
 constexpr int kF8Rows = 32 * kF8Waves; // query rows per workgroup
 constexpr int kF8BC = 128;              // keys per tile
 constexpr int kScaleOne = 127;          // E8M0 block scale 2^0
+constexpr int kF8Ahead = 2;             // MFMAs whose LDS operands are read ahead
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, kScaleOne);
@@ -101,9 +109,7 @@ struct F8Cfg {
     static constexpr int NK = kF8BC * KP / 1024;
     static constexpr int NV = D * VTP / 1024;
     static_assert(NK * 1024 == kF8BC * KP && NV * 1024 == D * VTP, "tiles are whole 1 KB blocks");
-    static constexpr int LPW = (NK + NV + kF8Waves - 1) / kF8Waves;
-    static constexpr int KST = kF8BC * KP;
-    static constexpr int STAGE = 1024 * kF8Waves * LPW;
+    static constexpr int LPW = (NK + NV + kF8Waves - 1) / kF8Waves; // loads per wave and tile
     static constexpr int OP = 2 * D + 16;    // bf16 O staging pitch
 };
 
@@ -114,10 +120,17 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     constexpr int KP = Cfg::KP, VTP = Cfg::VTP, OP = Cfg::OP;
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
     constexpr float kLimit = 256.0f; // P~ <= 2^8: within E4M3's range (448)
-    __shared__ __attribute__((aligned(16))) char stage0_raw[Cfg::STAGE];
-    __shared__ __attribute__((aligned(16))) char stage1_raw[Cfg::STAGE];
-    lds_char *const stage0 = (lds_char *)stage0_raw;
-    lds_char *const stage1 = (lds_char *)stage1_raw;
+    constexpr int KBYTES = NK * 1024;                    // K stage: the K tile
+    constexpr int VBYTES = (kF8Waves * LPW - NK) * 1024; // V^T stage: the tile and the spare blocks
+    static_assert(NV * 1024 <= VBYTES && KBYTES <= VBYTES, "stage sizes");
+    __shared__ __attribute__((aligned(16))) char ks0_raw[KBYTES];
+    __shared__ __attribute__((aligned(16))) char ks1_raw[KBYTES];
+    __shared__ __attribute__((aligned(16))) char vs0_raw[VBYTES];
+    __shared__ __attribute__((aligned(16))) char vs1_raw[VBYTES];
+    lds_char *const ks0 = (lds_char *)ks0_raw;
+    lds_char *const ks1 = (lds_char *)ks1_raw;
+    lds_char *const vs0 = (lds_char *)vs0_raw;
+    lds_char *const vs1 = (lds_char *)vs1_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -139,9 +152,10 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     const int kv_end = CAUSAL ? min(N, q0 + kF8Rows) : N;
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    // loader: load j of wave w fills 1 KB block w + 8 j of the stage; blocks
-    // [0, NK) hold the K tile (rows in MFMA row order), [NK, NK + NV) the V^T
-    // tile (feature rows, 128 keys each), the rest are spare
+    // loader: batch b = the K rows of tile b and the V^T columns of tile
+    // b - 1.  Load j of wave w fills 1 KB block w + 8 j: blocks [0, NK) go to
+    // the K stage (rows in MFMA row order), the rest to the V^T stage
+    // (feature rows of 128 keys, then spare blocks).
     uint32_t voff[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
@@ -160,20 +174,19 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         voff[j] = off;
     }
     const uint32_t vt_bytes = __builtin_amdgcn_readfirstlane((uint32_t)D * (uint32_t)Npad);
-    auto issue_tile = [&](int t, lds_char *st) {
-        const int k0 = t * BC;
+    auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
+        const int kk = b * BC, kv = max(b - 1, 0) * BC;
         const uint32_t k_bytes =
-            __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D));
-        // V^T rows hold keys up to Npad (zero-padded); a tile past the last loads nothing
-        const uint32_t v_bytes = k0 < kv_end ? vt_bytes : 0u;
+            __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D : 0));
+        // V^T rows hold keys up to Npad (zero-padded); past the last tile nothing is read
+        const uint32_t v_bytes = (b >= 1 && b - 1 < n_tiles) ? vt_bytes : 0u;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int blk = wave + kF8Waves * j; // wave-uniform
-            lds_char *dst = st + 1024 * blk;
-            if (blk >= NK && blk < NK + NV)
-                load_lds_16s(Vt, v_bytes, voff[j], (uint32_t)k0, dst);
+            if (blk < NK)
+                load_lds_16s(K + (int64_t)kk * D, k_bytes, voff[j], 0u, kd + 1024 * blk);
             else
-                load_lds_16s(K + (int64_t)k0 * D, k_bytes, voff[j], 0u, dst);
+                load_lds_16s(Vt, v_bytes, voff[j], (uint32_t)kv, vd + 1024 * (blk - NK));
         }
     };
 
@@ -202,118 +215,182 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     const int k_lane = r * KP + 32 * g;      // LDS row r of a K block, k half g
     const int v_lane = r * VTP + 16 * g;     // V^T row r of a feature block
 
-    auto tile = [&](int t, const lds_char *cur, lds_char *next) {
+    f32x16 s[KB];       // S^T of the wave's current tile
+    uint32_t pk[KB][4]; // its weights in E4M3: pk[kb][w] holds entries 4w .. 4w+3 of block kb
+
+    auto active = [&](int t) __attribute__((always_inline)) {
+        return (q0w < N) && (!CAUSAL || t * BC <= q0w + 31);
+    };
+    // S^T = K Q^T over the head dim in 64-wide steps
+    auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            s[kb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const lds_char *p = kst + k_lane + 32 * kb * KP + 64 * st;
+                const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
+                const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 16);
+                const i32x8 kv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                s[kb] = mfma8(kv, qf[st], s[kb]);
+            }
+        // kF8Ahead MFMAs' reads ahead, then two reads per MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8Ahead, 0);
+#pragma unroll
+        for (int n = 0; n < DS * KB - kF8Ahead; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kF8Ahead, 0);
+    };
+    // O^T += V^T P~^T over 64-key steps (blocks 2 s', 2 s' + 1)
+    auto accumulate = [&](const lds_char *vst) __attribute__((always_inline)) {
+        const lds_char *vs = vst + v_lane;
+#pragma unroll
+        for (int sp = 0; sp < KB / 2; ++sp)
+#pragma unroll
+            for (int b = 0; b < OB; ++b) {
+                const lds_char *p = vs + 32 * b * VTP + 64 * sp;
+                const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
+                const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 32);
+                const i32x8 vv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const i32x8 pb = {(int)pk[2 * sp][0], (int)pk[2 * sp][1], (int)pk[2 * sp][2], (int)pk[2 * sp][3],
+                                  (int)pk[2 * sp + 1][0], (int)pk[2 * sp + 1][1], (int)pk[2 * sp + 1][2],
+                                  (int)pk[2 * sp + 1][3]};
+                o[b] = mfma8(vv, pb, o[b]);
+            }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8Ahead, 0);
+#pragma unroll
+        for (int n = 0; n < OB * KB / 2 - kF8Ahead; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kF8Ahead, 0);
+    };
+    auto softmax = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BC;
-        const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
-        if (active) {
-            f32x16 s[KB];
+        // entry e of block kb, lane half g: key k0 + 32 kb + 16 g + e
+        if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
+            const int lim = (CAUSAL ? min(N, qi + 1) : N) - k0 - 16 * g;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                s[kb] = f32x16{};
 #pragma unroll
-            for (int st = 0; st < DS; ++st)
+                for (int e = 0; e < 16; ++e)
+                    s[kb][e] = (32 * kb + e < lim) ? s[kb][e] : -INFINITY;
+        }
+        // P~ = exp2(s c - m_ref) <= 2^8, summed in fp32, rounded to E4M3 for PV
+        float lt = 0.f;
+        auto exps = [&](float m_ref) __attribute__((always_inline)) {
+            lt = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const lds_char *p = cur + k_lane + 32 * kb * KP + 64 * st;
-                    const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
-                    const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 16);
-                    const i32x8 kv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    s[kb] = mfma8(kv, qf[st], s[kb]);
-                }
-            issue_tile(t + 1, next);
-            // entry e of block kb, lane half g: key k0 + 32 kb + 16 g + e
-            if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
-                const int lim = (CAUSAL ? min(N, qi + 1) : N) - k0 - 16 * g;
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                for (int w = 0; w < 4; ++w) {
+                    float p[4];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        s[kb][e] = (32 * kb + e < lim) ? s[kb][e] : -INFINITY;
-            }
-            // P~ = exp2(s c - m_ref) <= 2^8, summed in fp32, rounded to E4M3 for PV:
-            // pk[kb][w] holds entries 4w .. 4w+3 of block kb
-            uint32_t pk[KB][4];
-            float lt = 0.f;
-            auto exps = [&](float m_ref) {
-                lt = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        float p[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + u], c, -m_ref));
-                            lt += p[u];
-                        }
-                        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                        x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
-                        pk[kb][w] = (uint32_t)x;
+                    for (int u = 0; u < 4; ++u) {
+                        p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + u], c, -m_ref));
+                        lt += p[u];
                     }
-            };
-            bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
-            if (!move) {
-                exps(m_run);
-                move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
-            }
-            if (move) {
-                float mx = -INFINITY;
+                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
+                    pk[kb][w] = (uint32_t)x;
+                }
+        };
+        bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+        if (!move) {
+            exps(m_run);
+            move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
+        }
+        if (move) {
+            float mx = -INFINITY;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        mx = fmaxf(mx, s[kb][e]);
-                const float m_new = fmaxf(m_run, pair_max(mx) * c);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int b = 0; b < OB; ++b)
-                    o[b] *= alpha;
-                m_run = m_new;
-                exps(m_run == -INFINITY ? 0.f : m_run);
-            }
-            l_run += lt;
-            // O^T += V^T P~^T over 64-key steps (blocks 2 s', 2 s' + 1)
-            const lds_char *vs = cur + Cfg::KST + v_lane;
+                for (int e = 0; e < 16; ++e)
+                    mx = fmaxf(mx, s[kb][e]);
+            const float m_new = fmaxf(m_run, pair_max(mx) * c);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
             for (int b = 0; b < OB; ++b)
-#pragma unroll
-                for (int sp = 0; sp < KB / 2; ++sp) {
-                    const lds_char *p = vs + 32 * b * VTP + 64 * sp;
-                    const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
-                    const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 32);
-                    const i32x8 vv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    const i32x8 pb = {(int)pk[2 * sp][0], (int)pk[2 * sp][1], (int)pk[2 * sp][2], (int)pk[2 * sp][3],
-                                      (int)pk[2 * sp + 1][0], (int)pk[2 * sp + 1][1], (int)pk[2 * sp + 1][2],
-                                      (int)pk[2 * sp + 1][3]};
-                    o[b] = mfma8(vv, pb, o[b]);
-                }
-        } else {
-            issue_tile(t + 1, next);
+                o[b] *= alpha;
+            m_run = m_new;
+            exps(m_run == -INFINITY ? 0.f : m_run);
         }
-        wait_vmcnt<0>();
-        tile_barrier();
+        l_run += lt;
+    };
+    // M(t): O += P~(t-1) V(t-1), then S(t); X(t): softmax of S(t)
+    auto M = [&](int t, const lds_char *vprev, const lds_char *kcur) __attribute__((always_inline)) {
+        if (t >= 1 && t - 1 < n_tiles && active(t - 1))
+            accumulate(vprev);
+        if (t < n_tiles && active(t))
+            scores(kcur);
+    };
+    auto X = [&](int t) __attribute__((always_inline)) {
+        if (t >= 0 && t < n_tiles && active(t))
+            softmax(t);
     };
 
-    issue_tile(0, stage0);
+    // Ping-pong schedule (as in the 16-bit dense kernel): waves 4..7 run one
+    // phase behind waves 0..3, so on every SIMD one wave issues MFMAs while
+    // the other does its softmax.  Phase 2c: batch c + 1 goes out; group 0
+    // runs M(c), group 1 X(c - 1).  Phase 2c + 1: group 0 runs X(c), group 1
+    // M(c); batch c + 1 has landed at its end.
+    const int grp = wave >> 2;
+    issue_batch(0, ks0, vs1);
     wait_vmcnt<0>();
     tile_barrier();
-    int t = 0;
-    for (; t + 2 <= n_tiles; t += 2) {
-        tile(t, stage0, stage1);
-        tile(t + 1, stage1, stage0);
+    if (grp == 0) {
+        auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
+                        __attribute__((always_inline)) {
+            if (cc + 1 <= n_tiles)
+                issue_batch(cc + 1, kn, vn);
+            M(cc, vprev, kcur);
+            tile_barrier();
+            X(cc);
+            wait_vmcnt<0>();
+            tile_barrier();
+        };
+        int cc = 0;
+        for (; cc + 1 <= n_tiles; cc += 2) {
+            step(cc, ks1, vs0, vs1, ks0);
+            step(cc + 1, ks0, vs1, vs0, ks1);
+        }
+        if (cc <= n_tiles)
+            step(cc, ks1, vs0, vs1, ks0);
+    } else {
+        auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
+                        __attribute__((always_inline)) {
+            if (cc + 1 <= n_tiles)
+                issue_batch(cc + 1, kn, vn);
+            X(cc - 1);
+            tile_barrier();
+            M(cc, vprev, kcur);
+            wait_vmcnt<0>();
+            tile_barrier();
+        };
+        int cc = 0;
+        for (; cc + 1 <= n_tiles; cc += 2) {
+            step(cc, ks1, vs0, vs1, ks0);
+            step(cc + 1, ks0, vs1, vs0, ks1);
+        }
+        if (cc <= n_tiles)
+            step(cc, ks1, vs0, vs1, ks0);
     }
-    if (t < n_tiles)
-        tile(t, stage0, stage1);
 
     // epilogue: O = acc * v_descale / l in bf16, staged through LDS; lse
     const float l_tot = pair_sum(l_run);
     const float inv = a.v_descale / l_tot;
-    static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
-    tile_barrier();
-    lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
+    // every tile read is done; waves 2i and 2i + 1 stage their rows in stage array i
+    static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
+    const int sa = wave >> 1;
+    lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
+    lds_char *ow = own + (wave & 1) * 32 * OP;
     if (q0w < N) {
 #pragma unroll
         for (int b = 0; b < OB; ++b)
