@@ -34,6 +34,8 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -397,6 +399,11 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
         dka[b] = f32x16{};
     }
 
+    // One 64-query tile in two 32-query halves, staggered so that a half's
+    // softmax work (VALU) is issued between the MFMAs of the other half:
+    //   S, dP of half 0 | S, dP of half 1 + softmax of half 0
+    //   | dV, dK of half 0 + softmax of half 1 | dV, dK of half 1.
+    // Every accumulator still adds its terms in the same order.
     auto tile = [&](int t, const lds_char *cur, lds_char *next) {
         const int i0 = t * TQ;
         const bool active = (k0w < N) && (!CAUSAL || i0 + TQ - 1 >= k0w);
@@ -404,19 +411,16 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             const lds_char *qs = cur + q_lane;
             const lds_char *ds = cur + Tiles::NX * 1024 + q_lane;
             f32x16 s[QB], dp[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
+            // S = Q K^T and dP = dO V^T for query half qb
+            auto sdp = [&](int qb) __attribute__((always_inline)) {
                 s[qb] = f32x16{};
                 dp[qb] = f32x16{};
-            }
 #pragma unroll
-            for (int cc = 0; cc < DC; ++cc)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
+                for (int cc = 0; cc < DC; ++cc) {
                     s[qb] = E::mfma(lds_u32x4(qs + 32 * qb * P + 32 * cc), kf[cc], s[qb]);
                     dp[qb] = E::mfma(lds_u32x4(ds + 32 * qb * P + 32 * cc), vf[cc], dp[qb]);
                 }
-            issue(t + 1, next);
+            };
             // P = exp2(c2 s - log2(e) lse_i), dS = P (dP - Delta_i); causal: a query
             // before the key gets P = 0.  Query rows past N are zero (Q, dO, lse,
             // Delta), so their dS is 0 and their dO row adds nothing to dV.
@@ -424,8 +428,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             const int lim = kj - i0 - g; // entry (qb, i) is query i0 + 32 qb + 2 i + g
             const lds_char *stat = cur + STAT + 64 * g;
             uint32_t pp[QB][8], pd[QB][8];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            auto soft = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 128 * qb + 16 * m);
@@ -445,13 +448,13 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
                     pd[qb][2 * m] = E::pack(sv[0], sv[1]);
                     pd[qb][2 * m + 1] = E::pack(sv[2], sv[3]);
                 }
-            // dV^T += dO^T P and dK^T += Q^T dS
+            };
+            // dV^T += dO^T P and dK^T += Q^T dS for query half qb
             const lds_char *qt = cur + t_lane;
             const lds_char *dt = cur + Tiles::NX * 1024 + t_lane;
+            auto grad = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
-            for (int b = 0; b < OB; ++b)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
+                for (int b = 0; b < OB; ++b)
 #pragma unroll
                     for (int mm = 0; mm < 2; ++mm) {
                         const int off = (32 * qb + 16 * mm) * P + 64 * b;
@@ -460,6 +463,49 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
                         dva[b] = E::mfma(tr_read(dt + off, P), pv, dva[b]);
                         dka[b] = E::mfma(tr_read(qt + off, P), sv, dka[b]);
                     }
+            };
+            // MFMAs of one half with the softmax VALU work of the other in
+            // between: sixteen LDS reads ahead, then per MFMA its operand
+            // reads and four VALU instructions
+            auto interleave = [&](auto n_mfma, auto reads_per) __attribute__((always_inline)) {
+                constexpr int NM = decltype(n_mfma)::value, RP = decltype(reads_per)::value;
+                __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+                for (int n = 0; n < NM; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, RP, 0); // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                }
+            };
+            sdp(0);
+            // four operand reads ahead of the first half's S / dP MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int n = 0; n < 2 * DC - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            issue(t + 1, next);
+            __builtin_amdgcn_sched_barrier(0);
+            sdp(1);
+            soft(0);
+            interleave(std::integral_constant<int, 2 * DC>{}, std::integral_constant<int, 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            grad(0);
+            soft(1);
+            interleave(std::integral_constant<int, 4 * OB>{}, std::integral_constant<int, 2>{});
+            __builtin_amdgcn_sched_barrier(0);
+            grad(1);
+            // eight transposing reads (four MFMAs) ahead of the second half's
+            // dV / dK MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int n = 0; n < 4 * OB - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         } else {
             issue(t + 1, next);
         }
