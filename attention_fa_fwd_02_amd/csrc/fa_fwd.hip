@@ -159,6 +159,160 @@ struct MfmaCfg {
     static constexpr bool PINGPONG = WAVES == 8 && BC == 128;
 };
 
+// Per-lane byte offsets of the tile loader, two 16-bit offsets per register.
+// Load j of wave w fills 1 KB block b = w + WAVES j of a stage: blocks below
+// NK hold the K tile (row pitch KP), the next NV the V tile (pitch VP), the
+// rest are spare.  Lane l of a load writes stage byte 1024 b + 16 l; the
+// offset is that byte's position in the tile's rows of D 16-bit features
+// (a lane whose slot falls in a row's padding, or a spare block, re-reads the
+// row's first chunk; those bytes are never read back).
+template <int D>
+__device__ __forceinline__ void tile_offsets(uint32_t (&voff2)[(MfmaCfg<D>::LPW + 1) / 2], int wave, int lane) {
+    using Cfg = MfmaCfg<D>;
+    constexpr int W = Cfg::WAVES, NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW, KP = Cfg::KP, VP = Cfg::VP;
+    constexpr int KCH = D / 8; // 16-byte chunks per K/V row
+    static_assert(Cfg::BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
+#pragma unroll
+    for (int j = 0; j < (LPW + 1) / 2; ++j)
+        voff2[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int blk = wave + W * j;
+        const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
+        const int pitch = is_k ? KP : VP;
+        const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
+        const int chunk = (pos % pitch) / 16;
+        const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
+        voff2[j / 2] |= off << (16 * (j % 2));
+    }
+}
+
+// Q^T operand of the score MFMA: lane (r, g) holds q_qi[16c + 8g .. +7] for
+// step c (zero for rows at or past Nq); qneg flips the sign bits when the
+// scale is negative.
+template <int D>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[D / 16], const uint16_t *__restrict__ Q, int qi, int Nq, int g,
+                                       uint32_t qneg) {
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+        qf[cc] = qi < Nq ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
+        qf[cc] ^= qneg;
+    }
+}
+
+// Masks of one S^T tile: entry (kb, i) of lane half g is key k0 + 32 kb + 2 i + g.
+// mask_keys: keys at or past Nk, and (causal) keys after query qi + coff, get
+// score -inf.  mask_below: the same through one per-lane bound, lim = (first
+// invisible key) - k0 - g, compared with the compile-time 32 kb + 2 i, which
+// keeps the mask free of per-entry registers.
+template <int KB, bool CAUSAL>
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[KB], int k0, int Nk, int qi, int coff, int g) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 2 * i + g;
+            const bool vis = key < Nk && (!CAUSAL || key <= qi + coff);
+            s[kb][i] = vis ? s[kb][i] : -INFINITY;
+        }
+}
+template <int KB>
+__device__ __forceinline__ void mask_below(f32x16 (&s)[KB], int lim) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s[kb][i] = (32 * kb + 2 * i < lim) ? s[kb][i] : -INFINITY;
+}
+
+// Online softmax of one S^T tile against the running reference m_run
+// (log2 domain, c = |scale| log2 e): P~ = exp2(s c - m_run), summed into
+// l_run in fp32 and rounded into pk for the PV MFMA (pk[kb][j] holds entries
+// 2j, 2j + 1 of block kb).  The reference moves only when it is missing (the
+// first tile: no optimistic pass then) or some row's share of the tile's sum
+// exceeds 2^kTau, i.e. a score beat the reference by more than kTau (log2
+// units); P~ <= 2^kTau keeps fp32 far from overflow.  Then O and l are
+// rescaled to the row maximum and P~ is redone.
+template <typename E, int KB, int OB>
+__device__ __forceinline__ void online_softmax(f32x16 (&s)[KB], uint32_t (&pk)[KB][8], f32x16 (&o)[OB],
+                                               float &m_run, float &l_run, float c) {
+    constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8
+    float lt = 0.f;
+    auto exps = [&](float m_ref) __attribute__((always_inline)) {
+        lt = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
+                lt += p0 + p1;
+                pk[kb][i >> 1] = E::pack(p0, p1);
+            }
+    };
+    bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    if (!move) {
+        exps(m_run);
+        move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
+    }
+    if (move) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, s[kb][i]);
+        const float m_new = fmaxf(m_run, pair_max(mx) * c);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+            o[b] *= alpha;
+        m_run = m_new;
+        exps(m_run == -INFINITY ? 0.f : m_run);
+    }
+    l_run += lt;
+}
+
+// Epilogue of one wave: O / l rounded to the element type into the wave's
+// private LDS rows ow (pitch 2D + 16 bytes; o[b][i] is feature
+// 32b + 8(i/4) + 4g + i%4 of query qi), lse = (m + log2 l) ln 2, then the
+// rows are stored as 16-byte chunks covering whole cache lines.  Every wave
+// of the workgroup calls it (it holds a workgroup barrier).
+template <typename E, int D>
+__device__ __forceinline__ void store_o(const f32x16 (&o)[D / 32], float inv, float m_run, float l_tot,
+                                        lds_char *ow, uint16_t *__restrict__ O, float *__restrict__ LSE, int q0w,
+                                        int Nq, int lane) {
+    constexpr int OB = D / 32, KCH = D / 8, OP = 2 * D + 16;
+    const int r = lane & 31, g = lane >> 5, qi = q0w + r;
+    if (q0w < Nq) {
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const u32x2 w = {E::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
+                                 E::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
+                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
+            }
+        if (g == 0 && qi < Nq)
+            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    __syncthreads();
+    if (q0w < Nq) {
+        constexpr int kChunks = 32 * KCH; // 16-byte chunks in the wave's 32 rows
+#pragma unroll
+        for (int j = 0; j < kChunks / 64; ++j) {
+            const int ch = 64 * j + lane;
+            const int row = ch / KCH, col = ch % KCH;
+            const int q = q0w + row;
+            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
+            if (q < Nq)
+                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
+        }
+    }
+}
+
 template <typename E, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
@@ -168,9 +322,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     constexpr int KB = BC / 32; // 32-key MFMA blocks per tile
     constexpr int DC = D / 16;  // k-steps of the score MFMA
     constexpr int OB = D / 32;  // 32-feature blocks of O
-    constexpr int KCH = D / 8;  // 16-byte chunks per K/V row
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
-    constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8: deferred-rescale threshold
     // Two tile stages as separate LDS objects: the compiler can then tell that
     // the direct-to-LDS loads into one stage do not alias the reads of the
     // other, and does not wait for them before every LDS read.
@@ -257,24 +409,8 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     // unconditionally, also past the last tile, so that every wave issues the
     // same loads on every path.
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
-    // byte offset of the lane's 16 bytes from the tile's first row, two 16-bit
-    // offsets per register (a tile is at most 32 KB); spare blocks read the
-    // first row again
-    static_assert(BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
     uint32_t voff2[(LPW + 1) / 2];
-#pragma unroll
-    for (int j = 0; j < (LPW + 1) / 2; ++j)
-        voff2[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int blk = wave + W * j;
-        const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
-        const int pitch = is_k ? KP : VP;
-        const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
-        const int chunk = (pos % pitch) / 16;
-        const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
-        voff2[j / 2] |= off << (16 * (j % 2));
-    }
+    tile_offsets<D>(voff2, wave, lane);
     auto issue_tile = [&](int t, lds_char *st) {
         const int k0 = k_begin + t * BC;
         const uint32_t bytes =
@@ -287,7 +423,6 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
                         st + 1024 * (wave + W * j));
         }
     };
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     // --- per-lane LDS read bases --------------------------------------------
     // score MFMA A operand: row r of a 32-key block is key 8(r/8) + 2(r%4) + (r/4)%2,
@@ -300,11 +435,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 
     // --- Q^T operand: lane (r, g) holds q_{qi}[16c + 8g .. +7] for step c ---
     u32x4 qf[DC];
-#pragma unroll
-    for (int cc = 0; cc < DC; ++cc) {
-        qf[cc] = qi < Nq ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
-        qf[cc] ^= a.qneg;
-    }
+    load_q<D>(qf, Q, qi, Nq, g, a.qneg);
 
     f32x16 o[OB];
 #pragma unroll
@@ -349,70 +480,13 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
             issue_tile(t + 1, next);
             // masking: keys beyond Nk, and keys after the query when causal
             if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff)) {
-                if constexpr (VARLEN) {
-                    // entry (kb, i) is key k0 + g + e with e = 32 kb + 2 i; one
-                    // per-lane bound against the compile-time e keeps the mask
-                    // free of per-entry registers
-                    const int lim = CAUSAL ? min(Nk, qi + coff + 1) - k0 - g : Nk - k0 - g;
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            s[kb][i] = (32 * kb + 2 * i < lim) ? s[kb][i] : -INFINITY;
-                } else {
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = k0 + 32 * kb + 2 * i + g;
-                            const bool vis = key < Nk && (!CAUSAL || key <= qi + coff);
-                            s[kb][i] = vis ? s[kb][i] : -INFINITY;
-                        }
-                }
+                if constexpr (VARLEN)
+                    mask_below<KB>(s, (CAUSAL ? min(Nk, qi + coff + 1) : Nk) - k0 - g);
+                else
+                    mask_keys<KB, CAUSAL>(s, k0, Nk, qi, coff, g);
             }
-            // online softmax against the current reference m_ref:
-            // P~ = exp2(s*c - m_ref), summed in fp32, then rounded for the PV MFMA
             uint32_t pk[KB][8];
-            float lt = 0.f;
-            auto exps = [&](float m_ref) {
-                lt = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
-                        lt += p0 + p1;
-                        pk[kb][i >> 1] = E::pack(p0, p1);
-                    }
-            };
-            // The reference moves only when it is missing (first tile: no
-            // optimistic pass then) or some row's share exceeds 2^kTau, i.e. a
-            // score beat the reference by more than kTau (log2 units); P~ <=
-            // 2^kTau keeps fp32 far from overflow.  Then rescale O and l to the
-            // row maximum and redo P~.
-            bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
-            if (!move) {
-                exps(m_run);
-                move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
-            }
-            if (move) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        mx = fmaxf(mx, s[kb][i]);
-                const float m_new = fmaxf(m_run, pair_max(mx) * c);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int b = 0; b < OB; ++b)
-                    o[b] *= alpha;
-                m_run = m_new;
-                exps(m_run == -INFINITY ? 0.f : m_run);
-            }
-            l_run += lt;
+            online_softmax<E, KB, OB>(s, pk, o, m_run, l_run, c);
             // O^T += V^T P^T : o[b][i] accumulates feature 32b + 8(i/4) + 4g + i%4 of query qi
 #pragma unroll
             for (int b = 0; b < OB; ++b)
@@ -510,32 +584,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     const float inv = (VARLEN && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
     static_assert(4 * 32 * OP <= Cfg::STAGE, "four waves' O rows fit in one stage");
     tile_barrier();
-    lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP;
-    if (q0w < Nq) {
-#pragma unroll
-        for (int b = 0; b < OB; ++b)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const u32x2 w = {E::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
-                                 E::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
-                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
-            }
-        if (g == 0 && qi < Nq)
-            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    }
-    __syncthreads();
-    if (q0w < Nq) {
-        constexpr int kChunks = 32 * KCH; // 16-byte chunks in the wave's 32 rows
-#pragma unroll
-        for (int j = 0; j < kChunks / 64; ++j) {
-            const int ch = 64 * j + lane;
-            const int row = ch / KCH, col = ch % KCH;
-            const int q = q0w + row;
-            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
-            if (q < Nq)
-                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
-        }
-    }
+    store_o<E, D>(o, inv, m_run, l_tot, (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP, O, LSE, q0w, Nq, lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -565,13 +614,12 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     using Cfg = MfmaCfg<D>;
     static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
     constexpr int W = Cfg::WAVES, QBLK = Cfg::QBLK, BC = Cfg::BC;
-    constexpr int KB = BC / 32, DC = D / 16, OB = D / 32, KCH = D / 8;
+    constexpr int KB = BC / 32, DC = D / 16, OB = D / 32;
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
     constexpr int KBYTES = NK * 1024;               // K stage: the K tile
     constexpr int VBYTES = (W * LPW - NK) * 1024;   // V stage: the V tile and the spare blocks
     static_assert(NV * 1024 <= VBYTES && KBYTES <= VBYTES, "stage sizes");
-    constexpr float kLimit = 256.0f; // 2^kTau, kTau = 8: deferred-rescale threshold
     __shared__ __attribute__((aligned(16))) char ks0_raw[KBYTES];
     __shared__ __attribute__((aligned(16))) char ks1_raw[KBYTES];
     __shared__ __attribute__((aligned(16))) char vs0_raw[VBYTES];
@@ -609,21 +657,8 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     // stage, the rest to the V stage (the V tile, then spare blocks that
     // re-read the tile's first row).  Descriptors stop at kv_end: rows past it
     // read as zeros.
-    static_assert(BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
     uint32_t voff2[(LPW + 1) / 2];
-#pragma unroll
-    for (int j = 0; j < (LPW + 1) / 2; ++j)
-        voff2[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int blk = wave + W * j;
-        const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
-        const int pitch = is_k ? KP : VP;
-        const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
-        const int chunk = (pos % pitch) / 16;
-        const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
-        voff2[j / 2] |= off << (16 * (j % 2));
-    }
+    tile_offsets<D>(voff2, wave, lane);
     auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
         const int kk = b * BC, kv = max(b - 1, 0) * BC;
         const uint32_t kbytes =
@@ -640,16 +675,11 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
                 load_lds_16(V + (int64_t)kv * D, vbytes, off, vd + 1024 * (blk - NK));
         }
     };
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const int k_lane = (8 * (r >> 3) + 2 * (r & 3) + ((r >> 2) & 1)) * KP + 16 * g;
     const int v_lane = (g + 2 * ((lane >> 2) & 3)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
     u32x4 qf[DC];
-#pragma unroll
-    for (int cc = 0; cc < DC; ++cc) {
-        qf[cc] = qi < N ? *(const u32x4 *)(Q + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
-        qf[cc] ^= a.qneg;
-    }
+    load_q<D>(qf, Q, qi, N, g, a.qneg);
     f32x16 o[OB];
 #pragma unroll
     for (int b = 0; b < OB; ++b)
@@ -720,51 +750,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     auto softmax = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BC;
         // masking: keys beyond N, and keys after the query when causal
-        if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w)) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + 32 * kb + 2 * i + g;
-                    const bool vis = key < N && (!CAUSAL || key <= qi);
-                    s[kb][i] = vis ? s[kb][i] : -INFINITY;
-                }
-        }
-        float lt = 0.f;
-        auto exps = [&](float m_ref) __attribute__((always_inline)) {
-            lt = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_ref));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_ref));
-                    lt += p0 + p1;
-                    pk[kb][i >> 1] = E::pack(p0, p1);
-                }
-        };
-        bool move = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
-        if (!move) {
-            exps(m_run);
-            move = __builtin_amdgcn_ballot_w64(!(lt <= kLimit)) != 0;
-        }
-        if (move) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s[kb][i]);
-            const float m_new = fmaxf(m_run, pair_max(mx) * c);
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int b = 0; b < OB; ++b)
-                o[b] *= alpha;
-            m_run = m_new;
-            exps(m_run == -INFINITY ? 0.f : m_run);
-        }
-        l_run += lt;
+        if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w))
+            mask_keys<KB, CAUSAL>(s, k0, N, qi, 0, g);
+        online_softmax<E, KB, OB>(s, pk, o, m_run, l_run, c);
     };
     auto M = [&](int t, const lds_char *vprev, const lds_char *kcur) __attribute__((always_inline)) {
         if (t >= 1 && t - 1 < n_tiles && active(t - 1))
@@ -827,34 +815,8 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int sa = wave >> 1;
     lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
     const float l_tot = pair_sum(l_run);
-    const float inv = 1.0f / l_tot;
     static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
-    lds_char *ow = own + (wave & 1) * 32 * OP;
-    if (q0w < N) {
-#pragma unroll
-        for (int b = 0; b < OB; ++b)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const u32x2 w = {E::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
-                                 E::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
-                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
-            }
-        if (g == 0 && qi < N)
-            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    }
-    __syncthreads();
-    if (q0w < N) {
-        constexpr int kChunks = 32 * KCH;
-#pragma unroll
-        for (int j = 0; j < kChunks / 64; ++j) {
-            const int ch = 64 * j + lane;
-            const int row = ch / KCH, col = ch % KCH;
-            const int q = q0w + row;
-            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
-            if (q < N)
-                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
-        }
-    }
+    store_o<E, D>(o, 1.0f / l_tot, m_run, l_tot, own + (wave & 1) * 32 * OP, O, LSE, q0w, N, lane);
 }
 
 // ----------------------------------------------------------------------------
