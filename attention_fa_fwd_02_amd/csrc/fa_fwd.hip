@@ -313,6 +313,104 @@ __device__ __forceinline__ void store_o(const f32x16 (&o)[D / 32], float inv, fl
     }
 }
 
+// The fp32 partial result of a key split: O / l (0 for a row that saw no key
+// of the split, whose l is 0) and lse = (m + log2 l) ln 2 (-inf for such a
+// row).  STAGED: through the wave's private LDS rows ow (pitch 4D + 16 bytes)
+// as 16-byte chunks of whole rows, with a workgroup barrier (every wave
+// calls it); otherwise 16-byte stores straight from the accumulators.
+template <int D, bool STAGED>
+__device__ __forceinline__ void store_part(const f32x16 (&o)[D / 32], float m_run, float l_tot, lds_char *ow,
+                                           float *__restrict__ PO, float *__restrict__ PLSE, int q0w, int Nq,
+                                           int lane) {
+    constexpr int OB = D / 32, OP4 = 4 * D + 16;
+    const int r = lane & 31, g = lane >> 5, qi = q0w + r;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if constexpr (STAGED) {
+        if (q0w < Nq) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
+                                     o[b][4 * a4 + 3] * inv};
+                    *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
+                }
+            if (g == 0 && qi < Nq)
+                PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        }
+        __syncthreads();
+        if (q0w < Nq) {
+            constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
+#pragma unroll
+            for (int j = 0; j < kChunks / 64; ++j) {
+                const int ch = 64 * j + lane;
+                const int row = ch / (D / 4), col = ch % (D / 4);
+                const int q = q0w + row;
+                const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
+                if (q < Nq)
+                    *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
+            }
+        }
+    } else {
+        if (q0w < Nq && qi < Nq) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
+                                     o[b][4 * a4 + 3] * inv};
+                    *(f32x4 *)(PO + (int64_t)qi * D + 32 * b + 8 * a4 + 4 * g) = w;
+                }
+            if (g == 0)
+                PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        }
+    }
+}
+
+// One workgroup's share of [B, H, N, D] slices: a (slice, query block) pair,
+// and for a key split the split's keys [k_begin, kv_end) (whole key tiles,
+// cut at the last key any row of the block sees) in n_tiles key tiles.
+struct SliceBlock {
+    int bh, split; // slice and key split
+    int q0, q0w;   // first query row of the block / of this wave
+    int k_begin, kv_end, n_tiles;
+};
+template <int D, int MODE, bool CAUSAL>
+__device__ __forceinline__ SliceBlock slice_block(const FwdArgs &a, int wave) {
+    static_assert(MODE == kDense || MODE == kSplit, "square slices");
+    constexpr int QBLK = MfmaCfg<D>::QBLK, BC = MfmaCfg<D>::BC;
+    constexpr bool SPLIT = MODE == kSplit;
+    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    SliceBlock k;
+    // a key-split grid has n_splits rows per slice: (slice, split) = divmod(row)
+    k.bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
+    k.split = SPLIT ? wk.bh - k.bh * a.n_splits : 0;
+    k.q0 = wk.qb * QBLK;
+    k.q0w = k.q0 + 32 * wave;
+    k.k_begin = SPLIT ? k.split * a.split_keys : 0;
+    const int kv_vis = CAUSAL ? min(a.N, k.q0 + QBLK) : a.N;
+    k.kv_end = SPLIT ? min(kv_vis, k.k_begin + a.split_keys) : kv_vis;
+    k.n_tiles = SPLIT ? (k.kv_end > k.k_begin ? (k.kv_end - k.k_begin + BC - 1) / BC : 0)
+                      : (k.kv_end + BC - 1) / BC;
+    return k;
+}
+
+// A split block that sees no key of its split writes lse = -inf for its rows'
+// partial (their O partial is never read) and returns true: the workgroup
+// exits.
+template <int D, int MODE>
+__device__ __forceinline__ bool split_block_empty(const SliceBlock &k, const FwdArgs &a, int tid) {
+    constexpr int QBLK = MfmaCfg<D>::QBLK;
+    if constexpr (MODE == kSplit) {
+        if (k.n_tiles == 0) {
+            if (tid < QBLK && k.q0 + tid < a.N)
+                a.part_lse[k.split * a.part_rows + (int64_t)k.bh * a.N + k.q0 + tid] = -INFINITY;
+            return true;
+        }
+    }
+    return false;
+}
+
 template <typename E, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
@@ -529,55 +627,14 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     // --- epilogue: O / l staged through LDS (wave-private rows), lse ---------
     const float l_tot = pair_sum(l_run);
     if constexpr (SPLIT) {
-        // fp32 partial output; a row that sees no key of the split has l = 0
-        // and m = -inf: O = 0, lse = -inf
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
         float *__restrict__ PO = a.part_o + (split * a.part_rows + (int64_t)bh * a.N) * D;
         float *__restrict__ PLSE = a.part_lse + split * a.part_rows + (int64_t)bh * a.N;
-        if constexpr (4 * 32 * OP4 <= Cfg::STAGE) {
+        constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
+        constexpr bool STAGED = 4 * 32 * OP4 <= Cfg::STAGE; // four waves' fp32 rows fit in one stage
+        if constexpr (STAGED)
             tile_barrier();
-            lds_char *ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4;
-            if (q0w < Nq) {
-#pragma unroll
-                for (int b = 0; b < OB; ++b)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
-                                         o[b][4 * a4 + 3] * inv};
-                        *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w;
-                    }
-                if (g == 0 && qi < Nq)
-                    PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-            }
-            __syncthreads();
-            if (q0w < Nq) {
-                constexpr int kChunks = 32 * (D / 4); // 16-byte chunks in the wave's 32 fp32 rows
-#pragma unroll
-                for (int j = 0; j < kChunks / 64; ++j) {
-                    const int ch = 64 * j + lane;
-                    const int row = ch / (D / 4), col = ch % (D / 4);
-                    const int q = q0w + row;
-                    const f32x4 val = *(const __attribute__((address_space(3))) f32x4 *)(ow + row * OP4 + col * 16);
-                    if (q < Nq)
-                        *(f32x4 *)(PO + (int64_t)q * D + col * 4) = val;
-                }
-            }
-        } else {
-            // rows too wide to stage: 16-byte stores straight from the accumulators
-            if (q0w < Nq && qi < Nq) {
-#pragma unroll
-                for (int b = 0; b < OB; ++b)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const f32x4 w = {o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv, o[b][4 * a4 + 2] * inv,
-                                         o[b][4 * a4 + 3] * inv};
-                        *(f32x4 *)(PO + (int64_t)qi * D + 32 * b + 8 * a4 + 4 * g) = w;
-                    }
-                if (g == 0)
-                    PLSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-            }
-        }
+        store_part<D, STAGED>(o, m_run, l_tot, (wave < 4 ? stage0 : stage1) + (wave & 3) * 32 * OP4, PO, PLSE,
+                              q0w, Nq, lane);
         return;
     }
     // (packed sequences: a row that sees no key has l = 0 and gets O = 0, lse = -inf)
@@ -588,11 +645,12 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 }
 
 // ----------------------------------------------------------------------------
-// bf16 / fp16 MFMA kernel, ping-pong schedule ([B, H, N, D] slices, head dims
-// with 128-key tiles)
+// bf16 / fp16 MFMA kernel, ping-pong schedule ([B, H, N, D] slices, whole or
+// split over keys; head dims with 128-key tiles)
 // ----------------------------------------------------------------------------
 // Same tiles, operand layouts, masking and online softmax as
-// fa_fwd_mfma_kernel; only the order of work differs.  A wave's work on key
+// fa_fwd_mfma_kernel; only the order of work differs.  (Packed sequences stay
+// on fa_fwd_mfma_kernel: on their length mix this schedule measured slower.)  A wave's work on key
 // tile t splits into
 //   M(t): O += P(t-1) V(t-1), then S(t) = K(t) Q^T   (MFMA, LDS reads)
 //   X(t): mask and online softmax of S(t) into P(t)   (VALU)
@@ -609,11 +667,13 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 // 2t + 1 and V(t) in phases 2t + 2 and 2t + 3, so two K stages and two V
 // stages (separate LDS objects, so the loads into one are never waited for
 // before reads of another) hold every tile for as long as it is read.
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs a) {
+    constexpr bool SPLIT = MODE == kSplit;
     using Cfg = MfmaCfg<D>;
     static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
-    constexpr int W = Cfg::WAVES, QBLK = Cfg::QBLK, BC = Cfg::BC;
+    static_assert(MODE != kVarlen, "square [B, H, N, D] slices only");
+    constexpr int W = Cfg::WAVES, BC = Cfg::BC;
     constexpr int KB = BC / 32, DC = D / 16, OB = D / 32;
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
@@ -636,21 +696,22 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int r = lane & 31;
     const int g = lane >> 5;
 
-    // --- slice and query block ---------------------------------------------
-    const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+    // --- slice, query block, key range ----------------------------------------
+    const SliceBlock blk = slice_block<D, MODE, CAUSAL>(a, wave);
+    if (split_block_empty<D, MODE>(blk, a, tid))
+        return;
     const int N = a.N;
-    const int64_t off = (int64_t)wk.bh * N * D;
+    const int64_t off = (int64_t)blk.bh * N * D;
     const uint16_t *__restrict__ Q = (const uint16_t *)a.q + off;
     const uint16_t *__restrict__ K = (const uint16_t *)a.k + off;
     const uint16_t *__restrict__ V = (const uint16_t *)a.v + off;
     uint16_t *__restrict__ O = (uint16_t *)a.o + off;
-    float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
-    const int q0 = wk.qb * QBLK;
-    const int q0w = q0 + 32 * wave; // first query row of this wave
-    const int qi = q0w + r;         // this lane's query row
-    // keys [0, kv_end): all of them, or up to the block's last query when causal
-    const int kv_end = CAUSAL ? min(N, q0 + QBLK) : N;
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    float *__restrict__ LSE = a.lse + (int64_t)blk.bh * N;
+    const int q0w = blk.q0w; // first query row of this wave
+    const int qi = q0w + r;  // this lane's query row
+    // (k_begin is 0 unless split; stated so, the compiler keeps the register
+    // allocation of the whole-slice kernel)
+    const int k_begin = SPLIT ? blk.k_begin : 0, kv_end = blk.kv_end, n_tiles = blk.n_tiles;
 
     // --- loader: batch b = the K rows of tile b and the V rows of tile b - 1 --
     // Load j of wave w fills 1 KB block w + 8j: blocks below NK go to the K
@@ -660,7 +721,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     uint32_t voff2[(LPW + 1) / 2];
     tile_offsets<D>(voff2, wave, lane);
     auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
-        const int kk = b * BC, kv = max(b - 1, 0) * BC;
+        const int kk = k_begin + b * BC, kv = k_begin + max(b - 1, 0) * BC;
         const uint32_t kbytes =
             __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D * 2 : 0));
         const uint32_t vbytes = __builtin_amdgcn_readfirstlane(
@@ -692,7 +753,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
 
     // a tile is skipped by a wave none of whose rows sees any of its keys
     auto active = [&](int t) __attribute__((always_inline)) {
-        return (q0w < N) && (!CAUSAL || t * BC <= q0w + 31);
+        return (q0w < N) && (!CAUSAL || k_begin + t * BC <= q0w + 31);
     };
     // S^T = K Q^T : s[kb][i] = score(query qi, key k0 + 32kb + 2i + g)
     auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
@@ -748,7 +809,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int k0 = t * BC;
+        const int k0 = k_begin + t * BC;
         // masking: keys beyond N, and keys after the query when causal
         if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w))
             mask_keys<KB, CAUSAL>(s, k0, N, qi, 0, g);
@@ -815,6 +876,14 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int sa = wave >> 1;
     lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
     const float l_tot = pair_sum(l_run);
+    if constexpr (SPLIT) {
+        constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
+        static_assert(2 * 32 * OP4 <= KBYTES, "two waves' fp32 O rows fit in a stage array");
+        float *__restrict__ PO = a.part_o + (blk.split * a.part_rows + (int64_t)blk.bh * a.N) * D;
+        float *__restrict__ PLSE = a.part_lse + blk.split * a.part_rows + (int64_t)blk.bh * a.N;
+        store_part<D, true>(o, m_run, l_tot, own + (wave & 1) * 32 * OP4, PO, PLSE, q0w, N, lane);
+        return;
+    }
     static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
     store_o<E, D>(o, 1.0f / l_tot, m_run, l_tot, own + (wave & 1) * 32 * OP, O, LSE, q0w, N, lane);
 }
@@ -1073,10 +1142,10 @@ template <typename E, int D, int MODE>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     constexpr int T = MfmaCfg<D>::THREADS;
-    if constexpr (MODE == kDense && MfmaCfg<D>::PINGPONG) {
+    if constexpr (MODE != kVarlen && MfmaCfg<D>::PINGPONG) {
         if (causal)
-            return launch<fa_fwd_pp_kernel<E, D, true>, T>(nwg, 0, args, stream);
-        return launch<fa_fwd_pp_kernel<E, D, false>, T>(nwg, 0, args, stream);
+            return launch<fa_fwd_pp_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
+        return launch<fa_fwd_pp_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
     } else {
         if (causal)
             return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
