@@ -92,6 +92,17 @@ def device_inputs(B, H, N, D, dtype, sigma, seed=1004):
     return (q, k, v), tuple(up(x) for x in (q, k, v))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
     """The fp64 oracle, as it stands, on a bounded row sample of the same workload;
     also checks those rows of the GPU output.  Returns the JSON object."""
@@ -138,7 +149,11 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
     t, f, eo, el = run(rows_per_head, nheads)
     log("cpu oracle: %d heads x %d rows, %.2f s, %.3f GFLOP/s, %d threads; sampled GPU rows max|dO|=%.3g max|dlse|=%.3g"
         % (nheads, rows_per_head, t, f / t / 1e9, threads, eo, el))
+    # the oracle's work for every row of the workload (a causal row i has i + 1 keys)
+    full_flops = 4.0 * B * H * D * (N * (N + 1) / 2.0 if causal else float(N) * N)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "extrapolated_full_workload_s": round(full_flops / (f / t), 1),
             "sample": "%d heads x %d seeded query rows (all %d keys%s), fp64 three-pass oracle, %.1f s"
                       % (nheads, rows_per_head, N, ", causal prefix" if causal else "", t),
             "check_max_abs_dO": eo, "check_max_abs_dlse": el}
@@ -214,7 +229,8 @@ def bench_one(name, steps, warmup, copy_calibration=False):
         % (name, B, H, N, D, dtype, causal, " splits=%d" % n_splits if split else "", ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
            100 * achieved / peak, dtype))
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
-               kernel_ms=kern_ms, value=value, achieved=achieved, peak=peak, flops=flops)
+               kernel_ms=kern_ms, kernel_min_ms=per[0], kernel_median_ms=per[len(per) // 2], value=value,
+               achieved=achieved, peak=peak, flops=flops)
     # inputs and outputs stay alive for the CPU-oracle leg, which runs after all GPU timing
     return res, (host, (o, lse), B, H, N, D, dtype, causal)
 
@@ -407,7 +423,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(r["achieved"] / r["peak"], 4),
                      "traffic": traffic,
                      "kernel": "fa_fwd_pp_kernel<%s, D=%d, causal=%d>" % (r["dtype"], r["D"], r["causal"]),
-                     "kernel_avg_ms": round(r["kernel_ms"], 5)},
+                     "kernel_avg_ms": round(r["kernel_ms"], 5),
+                     "kernel_median_ms": round(r["kernel_median_ms"], 5),
+                     "kernel_min_ms": round(r["kernel_min_ms"], 5)},
         "cpu_baseline": r.get("cpu_baseline"),
     }
     print(json.dumps(out), flush=True)
