@@ -217,6 +217,11 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
 
     f32x16 s[KB];       // S^T of the wave's current tile
     uint32_t pk[KB][4]; // its weights in E4M3: pk[kb][w] holds entries 4w .. 4w+3 of block kb
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            pk[kb][w] = 0u;
 
     auto active = [&](int t) __attribute__((always_inline)) {
         return (q0w < N) && (!CAUSAL || t * BC <= q0w + 31);
@@ -296,7 +301,9 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
                         p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + u], c, -m_ref));
                         lt += p[u];
                     }
-                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    // both halves are written: the register's old value is passed
+                    // through only so that no zeroing move is needed
+                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], (int)pk[kb][w], false);
                     x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
                     pk[kb][w] = (uint32_t)x;
                 }
