@@ -159,7 +159,7 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
             "check_max_abs_dO": eo, "check_max_abs_dlse": el}
 
 
-def bench_one(name, steps, warmup, copy_calibration=False):
+def bench_one(name, steps, warmup, copy_calibration=False, flush=False):
     import torch
 
     import attention_fa_fwd_02_amd as fa
@@ -210,12 +210,18 @@ def bench_one(name, steps, warmup, copy_calibration=False):
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # cold-cache variant: a 1 GiB fill between calls evicts the inputs from L2 and
+    # the 256 MB Infinity Cache; only the per-call events count then
+    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     t_begin.record(stream)
     for i in range(steps):
+        if flush:
+            junk.fill_(i & 255)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     t_end.record(stream)
+    del junk
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
@@ -225,9 +231,13 @@ def bench_one(name, steps, warmup, copy_calibration=False):
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    log("%s: B%d H%d N%d D%d %s causal=%d%s  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
-        % (name, B, H, N, D, dtype, causal, " splits=%d" % n_splits if split else "", ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
-           100 * achieved / peak, dtype))
+    if flush:
+        log("%s, cold caches: B%d H%d N%d D%d %s causal=%d  kernel avg %.4f ms (min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
+            % (name, B, H, N, D, dtype, causal, kern_ms, per[0], per[len(per) // 2], achieved, 100 * achieved / peak, dtype))
+    else:
+        log("%s: B%d H%d N%d D%d %s causal=%d%s  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
+            % (name, B, H, N, D, dtype, causal, " splits=%d" % n_splits if split else "", ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
+               100 * achieved / peak, dtype))
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
                kernel_ms=kern_ms, kernel_min_ms=per[0], kernel_median_ms=per[len(per) // 2], value=value,
                achieved=achieved, peak=peak, flops=flops)
@@ -373,6 +383,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (for scaling HBM byte counters)")
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time the headline, both modes, with caches flushed before every call (stderr)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -397,6 +409,9 @@ def main():
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("fp8", "fp8_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
+    if args.flush:
+        for name in ("headline", "headline_causal"):
+            bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), flush=True)
     r = main_res
     if not args.no_cpu_baseline:
         r["cpu_baseline"] = cpu_baseline(*main_ctx)
