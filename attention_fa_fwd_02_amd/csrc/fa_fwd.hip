@@ -435,6 +435,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     const int r = lane & 31;
     const int g = lane >> 5;
 
+    // (the block geometry is written out here rather than shared with the
+    // ping-pong kernel's slice_block: routed through a shared helper, the
+    // packed-sequence instances were scheduled differently and ran 1-4% slower)
     const Work wk = VARLEN ? map_workgroup_strided(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL)
                            : map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
     // a key-split grid has n_splits rows per slice: (slice, split) = divmod(row)
