@@ -14,7 +14,8 @@
 //   fa_bwd_delta_kernel  Delta = rowsum(dO * O) in fp32 (memory-bound);
 //   fa_bwd_dq_kernel     one workgroup per 256 query rows (8 waves x 32 rows),
 //                        looping over 64-key tiles of K and V: S^T = K Q^T,
-//                        dP^T = V dO^T, dS, then dQ^T += K^T dS^T;
+//                        dP^T = V dO^T, dS, then dQ^T += K^T dS^T, the tile's
+//                        two 32-key halves staggered as in the dK/dV kernel;
 //   fa_bwd_dkdv_kernel   one workgroup per 128 keys (4 waves x 32 keys), looping
 //                        over 64-query tiles of Q and dO: S = Q K^T, dP = dO V^T,
 //                        dS, then dV^T += dO^T P and dK^T += Q^T dS.
@@ -226,6 +227,11 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
     for (int b = 0; b < OB; ++b)
         acc[b] = f32x16{};
 
+    // One 64-key tile in two 32-key halves, staggered so that a half's dS work
+    // (VALU) is issued between the MFMAs of the other half:
+    //   S, dP of half 0 | S, dP of half 1 + dS of half 0
+    //   | dQ of half 0 + dS of half 1 | dQ of half 1.
+    // Every accumulator still adds its terms in the same order.
     auto tile = [&](int t, const lds_char *cur, lds_char *next) {
         const int k0 = t * BC;
         const bool active = (q0w < N) && (!CAUSAL || k0 <= q0w + 31);
@@ -233,26 +239,22 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
             const lds_char *ks = cur + k_lane;
             const lds_char *vs = cur + Tiles::NX * 1024 + k_lane;
             f32x16 s[KB], dp[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+            // S^T = K Q^T and dP^T = V dO^T for key half kb
+            auto sdp = [&](int kb) __attribute__((always_inline)) {
                 s[kb] = f32x16{};
                 dp[kb] = f32x16{};
-            }
 #pragma unroll
-            for (int cc = 0; cc < DC; ++cc)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
+                for (int cc = 0; cc < DC; ++cc) {
                     s[kb] = E::mfma(lds_u32x4(ks + 32 * kb * P + 32 * cc), qf[cc], s[kb]);
                     dp[kb] = E::mfma(lds_u32x4(vs + 32 * kb * P + 32 * cc), df[cc], dp[kb]);
                 }
-            tiles.issue(K, V, (t + 1) * BC, kv_end, next, wave);
+            };
             // dS = P (dP - Delta), P = exp2(c2 s - log2(e) lse); causal: keys after
             // the query get P = 0 (rows past N are zero and contribute nothing)
             const bool diag = CAUSAL && k0 + BC - 1 > q0w;
             const int lim = qi - k0 - g; // entry (kb, i) is key k0 + 32 kb + 2 i + g
             uint32_t pk[KB][8];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            auto soft = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
                     float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, nl));
@@ -263,18 +265,60 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
                     }
                     pk[kb][i >> 1] = E::pack(p0 * (dp[kb][i] - dl), p1 * (dp[kb][i + 1] - dl));
                 }
-            // dQ^T += K^T dS^T
+            };
+            // dQ^T += K^T dS^T for key half kb
             const lds_char *kt = cur + t_lane;
+            auto grad = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-            for (int b = 0; b < OB; ++b)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                for (int b = 0; b < OB; ++b)
 #pragma unroll
                     for (int mm = 0; mm < 2; ++mm) {
                         const u32x4 kv = tr_read(kt + (32 * kb + 16 * mm) * P + 64 * b, P);
                         const u32x4 pb = {pk[kb][4 * mm], pk[kb][4 * mm + 1], pk[kb][4 * mm + 2], pk[kb][4 * mm + 3]};
                         acc[b] = E::mfma(kv, pb, acc[b]);
                     }
+            };
+            // MFMAs of one half with the VALU work of the other in between:
+            // four LDS reads ahead (the register file holds no more here), then
+            // per MFMA its operand reads and four VALU instructions
+            auto interleave = [&](auto n_mfma, auto reads_per) __attribute__((always_inline)) {
+                constexpr int NM = decltype(n_mfma)::value, RP = decltype(reads_per)::value;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int n = 0; n < NM; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, RP, 0); // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                }
+            };
+            sdp(0);
+            // four operand reads ahead of the first half's S / dP MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int n = 0; n < 2 * DC - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            tiles.issue(K, V, (t + 1) * BC, kv_end, next, wave);
+            __builtin_amdgcn_sched_barrier(0);
+            sdp(1);
+            soft(0);
+            interleave(std::integral_constant<int, 2 * DC>{}, std::integral_constant<int, 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            grad(0);
+            soft(1);
+            interleave(std::integral_constant<int, 2 * OB>{}, std::integral_constant<int, 2>{});
+            __builtin_amdgcn_sched_barrier(0);
+            grad(1);
+            // eight transposing reads (four MFMAs) ahead of the second half's dQ MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int n = 0; n < 2 * OB - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         } else {
             tiles.issue(K, V, (t + 1) * BC, kv_end, next, wave);
         }
