@@ -407,7 +407,7 @@ fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (dtype == FA_DTYPE_F32 || (D != 64 && D != 128))
+    if (dtype == FA_DTYPE_F32 || (D != 64 && D != 96 && D != 128))
         return FA_ERR_UNSUPPORTED;
     if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;

@@ -141,24 +141,32 @@ struct TilePair {
 // ----------------------------------------------------------------------------
 // Delta_i = dO_i . O_i (fp32), one row per D/8 lanes
 // ----------------------------------------------------------------------------
+// Lanes per row of the Delta kernel: the largest power of two dividing the
+// row's D / 8 sixteen-byte chunks (the row sum is a shuffle over them).
+constexpr int delta_lanes(int D) { return (D / 8) & -(D / 8); }
+
 template <typename E, int D>
 __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                            const uint16_t *__restrict__ dO,
                                                            float *__restrict__ delta, int64_t rows) {
-    constexpr int TPR = D / 8; // lanes per row (8 or 16)
+    constexpr int TPR = delta_lanes(D); // lanes per row (8, 4 or 16)
+    constexpr int CPL = D / 8 / TPR;    // 16-byte chunks per lane (1, 3 or 1)
     const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = item / TPR;
     const int c = (int)(item % TPR);
     float acc = 0.f;
     if (row < rows) {
-        const u32x4 ov = *(const u32x4 *)(O + row * D + 8 * c);
-        const u32x4 dv = *(const u32x4 *)(dO + row * D + 8 * c);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const f32x2 a = E::unpack(ov[w]);
-            const f32x2 b = E::unpack(dv[w]);
-            acc = __builtin_fmaf(a[0], b[0], acc);
-            acc = __builtin_fmaf(a[1], b[1], acc);
+        for (int j = 0; j < CPL; ++j) {
+            const u32x4 ov = *(const u32x4 *)(O + row * D + 8 * (c + TPR * j));
+            const u32x4 dv = *(const u32x4 *)(dO + row * D + 8 * (c + TPR * j));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2 a = E::unpack(ov[w]);
+                const f32x2 b = E::unpack(dv[w]);
+                acc = __builtin_fmaf(a[0], b[0], acc);
+                acc = __builtin_fmaf(a[1], b[1], acc);
+            }
         }
     }
     // sum over the TPR lanes of the row (aligned groups of a wave)
@@ -608,7 +616,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
 template <typename E, int D>
 hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
     const int64_t rows = BH * args.N;
-    const int64_t items = rows * (D / 8);
+    const int64_t items = rows * delta_lanes(D);
     hipLaunchKernelGGL((fa_bwd_delta_kernel<E, D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
                        (const uint16_t *)args.o, (const uint16_t *)args.dout, args.delta, rows);
     hipError_t err = hipGetLastError();
@@ -628,12 +636,19 @@ hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_
 
 } // namespace
 
+template <typename E>
+hipError_t launch_bwd_e(int D, bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
+    if (D == 64)
+        return launch_bwd_t<E, 64>(causal, BH, args, stream);
+    if (D == 96)
+        return launch_bwd_t<E, 96>(causal, BH, args, stream);
+    return launch_bwd_t<E, 128>(causal, BH, args, stream);
+}
+
 hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
     if (dtype == 1)
-        return D == 64 ? launch_bwd_t<Bf16, 64>(causal, BH, args, stream)
-                       : launch_bwd_t<Bf16, 128>(causal, BH, args, stream);
-    return D == 64 ? launch_bwd_t<F16, 64>(causal, BH, args, stream)
-                   : launch_bwd_t<F16, 128>(causal, BH, args, stream);
+        return launch_bwd_e<Bf16>(D, causal, BH, args, stream);
+    return launch_bwd_e<F16>(D, causal, BH, args, stream);
 }
 
 } // namespace fa

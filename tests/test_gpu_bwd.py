@@ -91,11 +91,17 @@ def check_bwd(B, H, N, D, dtype, causal, seed, scale=None, slices=None):
 
 
 @pytest.mark.parametrize("N", [1, 31, 64, 100, 255, 257, 600])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ragged(N, D, dtype, causal):
     check_bwd(1, 2, N, D, dtype, causal, seed=700 + N + D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d96_several_blocks(causal):
+    """D = 96 over several query and key blocks with a ragged tail (N = 1100)."""
+    check_bwd(1, 3, 1100, 96, "bf16", causal, seed=796)
 
 
 @pytest.mark.parametrize("causal", [False, True])
