@@ -292,15 +292,16 @@ def bench_varlen(name, steps, warmup):
 
 
 def bench_bwd(name, steps, warmup):
-    """fa_bwd on the headline shape (stderr line only).  FLOPs: the five
-    contractions of the backward pass, 10*B*H*N^2*D (2.5x the forward's count,
-    halved for causal); the kernels recompute S and dP once more (seven)."""
+    """fa_bwd on the headline shape, or at D = 96 for "bwd_d96*" (stderr line
+    only).  FLOPs: the five contractions of the backward pass, 10*B*H*N^2*D
+    (2.5x the forward's count, halved for causal); the kernels recompute S and
+    dP once more (seven)."""
     import torch
 
     import attention_fa_fwd_02_amd as fa
     import fa_inputs as fi
     causal = name.endswith("causal")
-    B, H, N, D, dtype = 4, 16, 4096, 128, "bf16"
+    B, H, N, D, dtype = 4, 16, 4096, 96 if name.startswith("bwd_d96") else 128, "bf16"
     host, (q, k, v) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0))
     _, (do, _, _) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0), seed=1004 + 7919)
     scale = 1.0 / math.sqrt(D)
@@ -405,7 +406,7 @@ def main():
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("varlen", "varlen_causal"):
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("bwd", "bwd_causal"):
+        for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("fp8", "fp8_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
