@@ -10,8 +10,8 @@ Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
 ``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_bwd``,
 ``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_fwd_fp8``,
 ``fa_fwd_fp8_workspace_bytes``, ``fa_check_fp8_args``, ``fa_status_string``,
-``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen``, ``bwd`` and
-``lse_merge`` are convenience wrappers that allocate outputs (and
+``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen``, ``bwd``,
+``fwd_fp8`` and ``lse_merge`` are convenience wrappers that allocate outputs (and
 workspaces) with torch (device memory and the current stream are all torch
 provides).
 """
@@ -27,7 +27,7 @@ __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INV
            "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
            "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
            "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_status_string",
-           "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "bwd", "lse_merge"]
+           "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "bwd", "fwd_fp8", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
