@@ -729,14 +729,18 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
             __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D * 2 : 0));
         const uint32_t vbytes = __builtin_amdgcn_readfirstlane(
             (uint32_t)(b >= 1 && b - 1 < n_tiles ? min(kv_end - kv, BC) * D * 2 : 0));
+        const uint16_t *const kb_ = K + (int64_t)kk * D;
+        const uint16_t *const vb_ = V + (int64_t)kv * D;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int blk = wave + W * j; // wave-uniform
             const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
-            if (blk < NK)
-                load_lds_16(K + (int64_t)kk * D, kbytes, off, kd + 1024 * blk);
-            else
-                load_lds_16(V + (int64_t)kv * D, vbytes, off, vd + 1024 * (blk - NK));
+            // K or V block chosen by selects, not branches
+            const bool isk = blk < NK;
+            const uint16_t *base = isk ? kb_ : vb_;
+            const uint32_t bytes = isk ? kbytes : vbytes;
+            lds_char *dst = isk ? kd + 1024 * blk : vd + 1024 * (blk - NK);
+            load_lds_16(base, bytes, off, dst);
         }
     };
     const int k_lane = (8 * (r >> 3) + 2 * (r & 3) + ((r >> 2) & 1)) * KP + 16 * g;
