@@ -180,13 +180,14 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
             __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D : 0));
         // V^T rows hold keys up to Npad (zero-padded); past the last tile nothing is read
         const uint32_t v_bytes = (b >= 1 && b - 1 < n_tiles) ? vt_bytes : 0u;
+        const uint8_t *const kb_ = (const uint8_t *)K + (int64_t)kk * D;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int blk = wave + kF8Waves * j; // wave-uniform
-            if (blk < NK)
-                load_lds_16s(K + (int64_t)kk * D, k_bytes, voff[j], 0u, kd + 1024 * blk);
-            else
-                load_lds_16s(Vt, v_bytes, voff[j], (uint32_t)kv, vd + 1024 * (blk - NK));
+            // K or V^T block chosen by selects, not branches
+            const bool isk = blk < NK;
+            load_lds_16s(isk ? (const void *)kb_ : (const void *)Vt, isk ? k_bytes : v_bytes, voff[j],
+                         isk ? 0u : (uint32_t)kv, isk ? kd + 1024 * blk : vd + 1024 * (blk - NK));
         }
     };
 
