@@ -9,7 +9,8 @@ Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
 ``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
 ``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_bwd``,
 ``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_fwd_fp8``,
-``fa_fwd_fp8_workspace_bytes``, ``fa_check_fp8_args``, ``fa_status_string``,
+``fa_fwd_fp8_workspace_bytes``, ``fa_check_fp8_args``, ``fa_fwd_kernel_name``,
+``fa_status_string``,
 ``fa_abi_version``.  ``fwd``, ``fwd_split``, ``fwd_varlen``, ``bwd``,
 ``fwd_fp8`` and ``lse_merge`` are convenience wrappers that allocate outputs (and
 workspaces) with torch (device memory and the current stream are all torch
@@ -26,7 +27,7 @@ __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INV
            "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
            "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
-           "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_status_string",
+           "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_fwd_kernel_name", "fa_status_string",
            "fa_abi_version", "fwd", "fwd_split", "fwd_varlen", "bwd", "fwd_fp8", "lse_merge"]
 
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
@@ -94,6 +95,8 @@ def load_library():
         lib.fa_check_fp8_args.restype = ctypes.c_int
         lib.fa_check_fp8_args.argtypes = [vp] * 5 + [i64] * 4 + [f32] * 4 + [ctypes.c_int, vp, ctypes.c_uint64,
                                                                             ctypes.c_char_p]
+        lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
+        lib.fa_fwd_kernel_name.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -104,6 +107,11 @@ def load_library():
 
 def fa_status_string(status: int) -> str:
     return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_fwd_kernel_name(B: int, H: int, N: int, D: int, causal: int, dtype: int, n_cus: int) -> str:
+    """Name of the kernel fa_fwd launches for these sizes ("" if it would reject them); host only."""
+    return load_library().fa_fwd_kernel_name(B, H, N, D, int(causal), dtype, n_cus).decode()
 
 
 def fa_abi_version() -> int:
@@ -216,6 +224,20 @@ def _dtype_code(t) -> int:
     return codes[t]
 
 
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output must be a contiguous device tensor of exactly the
+    shape and dtype the kernel writes, on the inputs' device: the library writes
+    through its raw pointer."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a device tensor on %s" % (name, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, not %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None, stream=None):
     """O, lse = softmax(scale * Q K^T) V for [B, H, N, D] CUDA tensors (torch, on a gfx950 device).
 
@@ -238,8 +260,12 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_out(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -287,10 +313,16 @@ def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, n_split
     need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on %s" % q.device)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_out(lse, "lse", (B, H, N), torch.float32, q.device)
     handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -330,8 +362,12 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: fl
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    else:
+        _check_out(lse, "lse", (H, total_q), torch.float32, q.device)
     handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -421,8 +457,12 @@ def lse_merge(part_o, part_lse, out_dtype=None, out=None, lse=None, stream=None)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty(part_o.shape[1:], dtype=out_dtype, device=part_o.device)
+    else:
+        _check_out(out, "out", part_o.shape[1:], out.dtype, part_o.device)
     if lse is None:
         lse = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_o.device)
+    else:
+        _check_out(lse, "lse", part_lse.shape[1:], torch.float32, part_o.device)
     handle = _stream_handle(stream, part_o.device)
     with torch.cuda.device(part_o.device):
         st = fa_lse_merge(part_o.data_ptr(), part_lse.data_ptr(), P, rows, D, out.data_ptr(),

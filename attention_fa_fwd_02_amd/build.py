@@ -1,9 +1,16 @@
-"""Build libfa.so in-tree with hipcc for gfx950 (cross-compiles without a GPU)."""
+"""Build libfa.so in-tree with hipcc for gfx950 (cross-compiles without a GPU).
+
+Each source is compiled to an object file in parallel, then the objects are
+linked into attention_fa_fwd_02_amd/libfa.so.  Every call recompiles.
+"""
 from __future__ import annotations
 
+import concurrent.futures
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,28 +28,48 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# the host pass does not know the packed-fp32 target feature; that note is harmless
+_NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into attention_fa_fwd_02_amd/libfa.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include")] + SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 target feature; that note is harmless
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    return res.returncode, err
+
+
+def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source into attention_fa_fwd_02_amd/libfa.so (always recompiles)."""
+    tmpdir = tempfile.mkdtemp(prefix="libfa_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in SOURCES]
+        cmds = [[HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", s, "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        workers = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            results = list(pool.map(_run, cmds))
+        for c, (rc, err) in zip(cmds, results):
+            if rc != 0:
+                raise RuntimeError("hipcc failed (%d) on %s:\n%s" % (rc, c[-3], err))
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, err = _run(link)
+        if rc != 0:
+            raise RuntimeError("link failed (%d):\n%s" % (rc, err))
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -84,6 +84,9 @@ bool mul_ok(uint64_t a, uint64_t b, uint64_t *out) {
     return true;
 }
 
+// a * b < lim for a, b >= 1 and lim >= 1, without forming the product.
+bool prod_below(int64_t a, int64_t b, int64_t lim) { return a <= (lim - 1) / b; }
+
 } // namespace
 
 extern "C" {
@@ -98,8 +101,9 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32 and the "
-               "backward pass), problem too large for one launch, too many "
+        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32, 64/96/128 "
+               "for the backward pass, 64/128 for FP8), fp32 backward, problem too large for "
+               "one launch, too many "
                "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
                "device is not gfx950)";
     case FA_ERR_HIP:
@@ -107,6 +111,18 @@ const char *fa_status_string(int status) {
     default:
         return "unknown status";
     }
+}
+
+const char *fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                               int64_t n_cus) {
+    // any distinct, aligned addresses: only the sizes and flags are checked
+    const uintptr_t base = uintptr_t(1) << 60, step = uintptr_t(1) << 56;
+    const void *q = (const void *)base, *k = (const void *)(base + step), *v = (const void *)(base + 2 * step);
+    void *o = (void *)(base + 3 * step);
+    float *lse = (float *)(base + 4 * step);
+    if (n_cus < 1 || fa_check_args(q, k, v, o, lse, B, H, N, D, 0.f, causal, dtype, nullptr) != FA_OK)
+        return "";
+    return fa::fwd_kernel_name(dtype, (int)D, causal != 0, fa::kDense);
 }
 
 fa_status fa_check_args(const void *q, const void *k, const void *v, const void *o,
@@ -129,10 +145,12 @@ fa_status fa_check_args(const void *q, const void *k, const void *v, const void 
     if (!fwd_head_dim_ok(D, dtype))
         return FA_ERR_UNSUPPORTED;
     // size limits: rows per launch and bytes per tensor
-    if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
+    // B, H < 2^31 keep B * H (< 2^62) exact; the products are then compared
+    // against their limits without being formed
+    if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 31) || H >= (int64_t(1) << 31))
         return FA_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
-    if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
+    if (BH >= (int64_t(1) << 36) || !prod_below(BH, N, int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;
     const int64_t n_qblk = (N + fa::query_block(D) - 1) / fa::query_block(D);
     // the dispatch grid is counted in work-items (32-bit): up to 512 per workgroup
@@ -330,10 +348,10 @@ fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const v
     if (D != 64 && D != 128)
         return FA_ERR_UNSUPPORTED;
     // V^T rows are addressed with 32-bit offsets: D * Npad < 2^32
-    if (N >= (int64_t(1) << 24) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
+    if (N >= (int64_t(1) << 24) || B >= (int64_t(1) << 31) || H >= (int64_t(1) << 31))
         return FA_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
-    if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
+    if (BH >= (int64_t(1) << 36) || !prod_below(BH, N, int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;
     if (BH * ((N + 255) / 256) >= (int64_t(1) << 23) || BH >= (int64_t(1) << 16))
         return FA_ERR_UNSUPPORTED;
@@ -409,10 +427,12 @@ fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if (dtype == FA_DTYPE_F32 || (D != 64 && D != 96 && D != 128))
         return FA_ERR_UNSUPPORTED;
-    if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 36) || H >= (int64_t(1) << 36))
+    // B, H < 2^31 keep B * H (< 2^62) exact; the products are then compared
+    // against their limits without being formed
+    if (N >= (int64_t(1) << 30) || B >= (int64_t(1) << 31) || H >= (int64_t(1) << 31))
         return FA_ERR_UNSUPPORTED;
     const int64_t BH = B * H;
-    if (BH >= (int64_t(1) << 36) || BH * N >= (int64_t(1) << 36))
+    if (BH >= (int64_t(1) << 36) || !prod_below(BH, N, int64_t(1) << 36))
         return FA_ERR_UNSUPPORTED;
     if (BH * ((N + 127) / 128) >= (int64_t(1) << 23))
         return FA_ERR_UNSUPPORTED;

@@ -66,6 +66,8 @@
 #include "fa_internal.h"
 
 #include <atomic>
+#include <cstdio>
+#include <mutex>
 
 namespace fa {
 namespace {
@@ -1193,6 +1195,36 @@ hipError_t launch_dtype(int dtype, int D, bool causal, int64_t nwg, const FwdArg
 }
 
 } // namespace
+
+const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode) {
+    // every (dtype, head dim, causal, mode) the dispatch below can reach, named
+    // as the profiler demangles the template instance
+    static char names[3][5][2][3][96];
+    static std::once_flag once;
+    static const int dims[5] = {64, 96, 128, 192, 256};
+    std::call_once(once, [] {
+        for (int t = 0; t < 3; ++t)
+            for (int di = 0; di < 5; ++di)
+                for (int c = 0; c < 2; ++c)
+                    for (int m = 0; m < 3; ++m) {
+                        const int d = dims[di];
+                        const char *cs = c ? "true" : "false";
+                        if (t == 0)
+                            snprintf(names[t][di][c][m], 96, "fa_fwd_f32_kernel<%d, %s, %d>", d, cs, m);
+                        else
+                            snprintf(names[t][di][c][m], 96, "%s<%s, %d, %s, %d>",
+                                     (m != kVarlen && d <= 128) ? "fa_fwd_pp_kernel" : "fa_fwd_mfma_kernel",
+                                     t == 1 ? "Bf16" : "F16", d, cs, m);
+                    }
+    });
+    int di = -1;
+    for (int i = 0; i < 5; ++i)
+        if (dims[i] == D)
+            di = i;
+    if (dtype < 0 || dtype > 2 || di < 0 || (int)mode < 0 || (int)mode > 2)
+        return "";
+    return names[dtype][di][causal ? 1 : 0][(int)mode];
+}
 
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
                       const FwdArgs &args, hipStream_t stream) {

@@ -51,6 +51,10 @@ constexpr int query_block(int64_t D) { return D > 192 ? 128 : 256; }
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
                       const FwdArgs &args, hipStream_t stream);
 
+// Name of the kernel launch_fwd runs for these arguments (static string; ""
+// for a combination it cannot launch).
+const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode);
+
 // FP8 (E4M3) forward arguments, passed by value.
 struct Fp8Args {
     const void *q;      // [B*H][N][D] E4M3

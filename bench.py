@@ -5,6 +5,13 @@ Q/K/V tiles -> scores -> online softmax -> P V -> O and lse), inputs already
 resident in HBM.  Default workload: B4 H16 N4096 D128, bf16, non-causal.
 Throughput counts 4*B*H*N^2*D FLOPs per step (half for causal).
 
+The default run also times every other configuration of the five synthetic
+workloads (tiny fp32; small bf16 both modes and fp32; the headline shape
+causal; wide D = 64; long-context causal) with the same step and warm-up
+counts and reports them in the JSON line's "workloads" object.  Warm-up runs
+at least --warmup steps and at least --warm-seconds of GPU work, so that the
+clocks have settled before the timed steps.
+
 Prints ONE JSON line on stdout; details go to stderr.
 """
 from __future__ import annotations
@@ -44,6 +51,11 @@ WORKLOADS = {
     "few_heads": (1, 2, 8192, 128, "bf16", False, (1.0, 1.0, 1.0)),
     "few_heads_causal": (1, 2, 8192, 128, "bf16", True, (1.0, 1.0, 1.0)),
 }
+# the configurations of the five synthetic workloads, in order, with their labels
+CONFIG_SET = [("tiny_f32", "C1 tiny fp32"), ("small", "C2 small bf16"), ("small_causal", "C2 small bf16 causal"),
+              ("small_f32", "C2 small fp32"), ("headline", "C3 headline bf16"),
+              ("headline_causal", "C3 headline bf16 causal"), ("wide", "C4 wide D64 bf16"),
+              ("long_causal", "C5 long-context causal bf16")]
 # the same workloads through fa_fwd_split (key splits + lse merge; split count
 # from fa_fwd_split_choose for the device's compute units)
 SPLIT_WORKLOADS = {"few_heads_split": "few_heads", "few_heads_causal_split": "few_heads_causal"}
@@ -152,6 +164,8 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
     # the oracle's work for every row of the workload (a causal row i has i + 1 keys)
     full_flops = 4.0 * B * H * D * (N * (N + 1) / 2.0 if causal else float(N) * N)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cores_note": "oracle threads used (the job's CPU share is 16 cores per GPU)",
+            "host_cores": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model(),
             "extrapolated_full_workload_s": round(full_flops / (f / t), 1),
             "sample": "%d heads x %d seeded query rows (all %d keys%s), fp64 three-pass oracle, %.1f s"
@@ -159,7 +173,22 @@ def cpu_baseline(host_qkv, dev_out, B, H, N, D, dtype, causal, budget_s=15.0):
             "check_max_abs_dO": eo, "check_max_abs_dlse": el}
 
 
-def bench_one(name, steps, warmup, copy_calibration=False, flush=False):
+def warm_up(step, warmup, warm_seconds):
+    """At least `warmup` steps and at least `warm_seconds` of wall time, in
+    synchronised chunks; returns the number of steps run."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    chunk = max(1, min(warmup, 50)) if warmup > 0 else 10
+    while n < warmup or time.perf_counter() - t0 < warm_seconds:
+        for _ in range(chunk):
+            step()
+        n += chunk
+        torch.cuda.synchronize()
+    return n
+
+
+def bench_one(name, steps, warmup, copy_calibration=False, flush=False, warm_seconds=0.0):
     import torch
 
     import attention_fa_fwd_02_amd as fa
@@ -202,9 +231,7 @@ def bench_one(name, steps, warmup, copy_calibration=False, flush=False):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm_up(step, warmup, warm_seconds)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -238,9 +265,13 @@ def bench_one(name, steps, warmup, copy_calibration=False, flush=False):
         log("%s: B%d H%d N%d D%d %s causal=%d%s  step %.4f ms (kernel avg %.4f, min %.4f, median %.4f)  %.1f TFLOP/s  %.1f%% of %s peak"
             % (name, B, H, N, D, dtype, causal, " splits=%d" % n_splits if split else "", ms_per_step, kern_ms, per[0], per[len(per) // 2], value,
                100 * achieved / peak, dtype))
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    kernel = fa.fa_fwd_kernel_name(B, H, N, D, int(causal), code, n_cus)
+    if split:
+        kernel = "%s (%d splits) + fa_merge_kernel" % (kernel.replace(", 0>", ", 1>"), n_splits)
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
                kernel_ms=kern_ms, kernel_min_ms=per[0], kernel_median_ms=per[len(per) // 2], value=value,
-               achieved=achieved, peak=peak, flops=flops)
+               achieved=achieved, peak=peak, flops=flops, kernel=kernel, warmup_steps_run=n_warm)
     # inputs and outputs stay alive for the CPU-oracle leg, which runs after all GPU timing
     return res, (host, (o, lse), B, H, N, D, dtype, causal)
 
@@ -380,6 +411,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS) + sorted(SPLIT_WORKLOADS))
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="minimum warm-up wall time before the timed steps (on top of --warmup steps)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only --workload (no per-configuration object; for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (for scaling HBM byte counters)")
@@ -397,7 +432,26 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    main_res, main_ctx = bench_one(args.workload, args.steps, args.warmup, args.copy_calibration)
+    main_res, main_ctx = bench_one(args.workload, args.steps, args.warmup, args.copy_calibration,
+                                   warm_seconds=args.warm_seconds)
+    workloads = None
+    if not args.no_workloads:
+        # every configuration of the five workloads, same step and warm-up counts
+        workloads = {}
+        for name, label in CONFIG_SET:
+            if name == args.workload:
+                r = main_res
+            else:
+                r, _ = bench_one(name, args.steps, args.warmup, warm_seconds=min(args.warm_seconds, 0.5))
+            workloads[name] = {
+                "label": label,
+                "config": "B%d H%d N%d D%d %s %s" % (r["B"], r["H"], r["N"], r["D"], r["dtype"],
+                                                   "causal" if r["causal"] else "non-causal"),
+                "tflops": round(r["value"], 3), "ms_per_step": round(r["ms_per_step"], 5),
+                "achieved": round(r["achieved"], 3), "peak": r["peak"], "peak_dtype": r["dtype"],
+                "frac": round(r["achieved"] / r["peak"], 4), "kernel": r["kernel"],
+                "kernel_avg_ms": round(r["kernel_ms"], 5), "kernel_median_ms": round(r["kernel_median_ms"], 5),
+                "kernel_min_ms": round(r["kernel_min_ms"], 5)}
     if args.all:
         # every GPU timing comes before the CPU-oracle leg, whose minutes of host
         # work would otherwise leave the GPU idle (and down-clocked) right before
@@ -438,12 +492,14 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["achieved"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["achieved"] / r["peak"], 4),
                      "traffic": traffic,
-                     "kernel": "fa_fwd_pp_kernel<%s, D=%d, causal=%d>" % (r["dtype"], r["D"], r["causal"]),
+                     "kernel": r["kernel"],
                      "kernel_avg_ms": round(r["kernel_ms"], 5),
                      "kernel_median_ms": round(r["kernel_median_ms"], 5),
                      "kernel_min_ms": round(r["kernel_min_ms"], 5)},
         "cpu_baseline": r.get("cpu_baseline"),
     }
+    if workloads is not None:
+        out["workloads"] = workloads
     print(json.dumps(out), flush=True)
 
 

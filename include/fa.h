@@ -78,9 +78,10 @@ typedef struct ihipStream_t *fa_stream_t;
  * scale, causal not 0/1, an unknown dtype, q/k/v/o not 16-byte aligned,
  * lse not 4-byte aligned, or o/lse overlapping each other or any input;
  * FA_ERR_UNSUPPORTED for a head dim outside the list above, a problem too
- * large for one launch (N >= 2^30, B*H*N >= 2^36, or B*H*ceil(N/R) >= 2^23
- * with R the workgroup's query rows), or a current device that is not gfx950.  FA_ERR_HIP when a device query or
- * the launch fails.  The call returns without waiting for the kernel;
+ * large for one launch (N >= 2^30, B or H >= 2^31, B*H*N >= 2^36, or
+ * B*H*ceil(N/R) >= 2^23 with R the workgroup's query rows), or a current
+ * device that is not gfx950.  FA_ERR_HIP when a device query or the launch
+ * fails.  The call returns without waiting for the kernel;
  * faults during execution surface at the caller's next synchronisation,
  * as usual for HIP.
  */
@@ -371,6 +372,17 @@ fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const v
                             const float *lse, const void *dq, const void *dk, const void *dv, int64_t B,
                             int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype,
                             const void *workspace, uint64_t workspace_bytes, const char *arch);
+
+/*
+ * fa_fwd_kernel_name -- the name of the forward kernel fa_fwd would launch
+ * for these sizes on a device with n_cus compute units, in the form
+ * rocprofv3 reports it (template arguments included), e.g.
+ * "fa_fwd_pp_kernel<Bf16, 128, false, 0>".  Host only (no HIP call); for
+ * profiles and reports.  Returns "" when fa_fwd would reject the sizes or
+ * the flags.  The string is static (never NULL).
+ */
+const char *fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                               int64_t n_cus);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -9,12 +9,12 @@ on deliberately broken variants of it (each must fail at least one pin).
 Facts used (cited by page title and section):
   * every row of P is a probability distribution -- KingOfEgg's
     FlashAttention v1 post, section 1.1;
-  * subtracting the row maximum does not change softmax, and the tiled
-    online recurrence (running max m, running exp-sum l, accumulator O
-    rescaled by exp(m_old - m_new), one division by l at the end) reaches
-    the same result as the materialising computation -- "08 ·
-    FlashAttention" parts 2-3; lesson 13 core concept 4 and its fill-in
-    exercise; pwwt.cn essay section 2.2;
+  * subtracting the row maximum does not change softmax, and a tiled
+    computation that keeps per-block statistics (maximum m, exp-sum l,
+    unnormalised output) and rescales them by exp(m_old - m_new) when they
+    are combined, dividing by l once at the end, reaches the same result as
+    the materialising computation -- "08 · FlashAttention" parts 2-3;
+    lesson 13 core concept 4; pwwt.cn essay section 2.2;
   * the per-step normalised merge of the original Algorithm 1 (O kept
     normalised after every key block) -- KingOfEgg's post, sections 2 and
     4.3;
@@ -33,40 +33,74 @@ import numpy as np
 # Independent recomputations (not the oracle's three-pass structure)
 # --------------------------------------------------------------------------
 
-def blocked_online(q, k, v, scale, causal, br, bc):
-    """Q-outer / KV-inner tiled forward with online softmax and deferred 1/l.
+def block_stats(s, vb):
+    """Statistics of one block of scores s [rows, keys] over value rows vb:
+    the block's row maximum m, its exp-sum l = sum_j e^(s_j - m) and the
+    unnormalised output A = sum_j e^(s_j - m) v_j.  A row with no visible key
+    (every score -inf) is the empty block (m, l, A) = (-inf, 0, 0)."""
+    m = s.max(axis=1)
+    has = np.isfinite(m)
+    w = np.exp(s - np.where(has, m, 0.0)[:, None])
+    w = np.where(has[:, None], w, 0.0)
+    return m, w.sum(axis=1), w @ vb
 
-    For each block of br query rows the state (m, l, acc) starts at
-    (-inf, 0, 0); each block of bc keys updates it: the running max takes the
-    block's row max, the old sum and accumulator are multiplied by
-    exp(m_old - m_new), the block's weights exp(s - m_new) are added; after
-    the last key block acc / l is the output and m + ln l the logsumexp.
-    """
+
+def merge_stats(x, y, mutation=None):
+    """Combine the statistics of two disjoint key sets.  The softmax sums over
+    their union are exact sums of the two parts once both are referred to the
+    common maximum m = max(m_x, m_y): l = l_x e^(m_x - m) + l_y e^(m_y - m),
+    and the same factors scale A.  The operation is associative, so the key
+    blocks can be combined in any grouping.  (`mutation` plants a mistake for
+    the tests that must catch it.)"""
+    (mx, lx, ax), (my, ly, ay) = x, y
+    m = np.maximum(mx, my)
+    safe = np.where(np.isfinite(m), m, 0.0)
+
+    def factor(mp):
+        if mutation == "no_rescale":
+            return np.where(np.isfinite(mp), 1.0, 0.0)
+        e = (safe - mp) if mutation == "flipped_exponent" else (mp - safe)
+        return np.where(np.isfinite(mp), np.exp(e), 0.0)
+
+    fx, fy = factor(mx), factor(my)
+    return m, lx * fx + ly * fy, ax * fx[:, None] + ay * fy[:, None]
+
+
+def blocked_tree(q, k, v, scale, causal, br, bc, mutation=None):
+    """Tiled forward from per-block statistics: every (query block of br rows,
+    key block of bc keys) pair is reduced to (m, l, A) on its own, the key
+    blocks of a query block are combined pairwise in a balanced tree with
+    merge_stats, and only then O = A / l and lse = m + ln l.  Nothing here
+    runs left to right over the keys, so it checks the exactness of tiling
+    without repeating the running-state recurrence.  mutation="block_softmax"
+    normalises each key block on its own and averages them (lesson 13 lists
+    "softmax each block and concatenate" as a disqualifying misconception)."""
     n, d = q.shape
     nk = k.shape[0]
     o = np.zeros((n, d))
     lse = np.zeros(n)
     for r0 in range(0, n, br):
         rows = np.arange(r0, min(n, r0 + br))
-        m_run = np.full(rows.size, -np.inf)
-        l_run = np.zeros(rows.size)
-        acc = np.zeros((rows.size, d))
+        parts = []
         for c0 in range(0, nk, bc):
             cols = np.arange(c0, min(nk, c0 + bc))
             s = scale * (q[rows] @ k[cols].T)
             if causal:
                 s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
-            blk_max = s.max(axis=1)
-            m_new = np.maximum(m_run, blk_max)
-            # rows that have seen no visible key yet keep m = -inf; avoid inf - inf
-            safe = np.where(np.isfinite(m_new), m_new, 0.0)
-            alpha = np.where(np.isfinite(m_run), np.exp(m_run - safe), 0.0)
-            w = np.exp(s - safe[:, None])
-            l_run = l_run * alpha + w.sum(axis=1)
-            acc = acc * alpha[:, None] + w @ v[cols]
-            m_run = m_new
-        o[rows] = acc / l_run[:, None]
-        lse[rows] = m_run + np.log(l_run)
+            parts.append(block_stats(s, v[cols]))
+        if mutation == "block_softmax":
+            outs = [a / np.where(l > 0, l, 1.0)[:, None] for (_, l, a) in parts]
+            o[rows] = sum(outs) / len(outs)
+            lse[rows] = np.nan
+            continue
+        while len(parts) > 1:
+            nxt = [merge_stats(parts[i], parts[i + 1], mutation) for i in range(0, len(parts) - 1, 2)]
+            if len(parts) % 2:
+                nxt.append(parts[-1])
+            parts = nxt
+        m, l, a = parts[0]
+        o[rows] = a / l[:, None]
+        lse[rows] = m + np.log(l)
     return o, lse
 
 
@@ -264,9 +298,9 @@ def pin_symmetry(attn):
 
 
 def pin_blocked(attn):
-    """The tiled online-softmax forward (Q-outer, deferred 1/l) and the
-    per-step normalised merge reach the same result for several tile shapes,
-    including tiles that do not divide N."""
+    """The tiled forward assembled from per-block statistics (tree merge,
+    deferred 1/l) and the per-step normalised merge reach the same result for
+    several tile shapes, including tiles that do not divide N."""
     rng = np.random.default_rng(17)
     for (n, d) in ((100, 8), (64, 16)):
         for causal in (False, True):
@@ -274,7 +308,7 @@ def pin_blocked(attn):
             sc = 1.0 / math.sqrt(d)
             o, lse = attn(q, k, v, sc, causal)
             for (br, bc) in ((1, 1), (16, 32), (32, 16), (n, n), (7, 13)):
-                ob, lb = blocked_online(q, k, v, sc, causal, br, bc)
+                ob, lb = blocked_tree(q, k, v, sc, causal, br, bc)
                 np.testing.assert_allclose(ob, o, rtol=0, atol=1e-12)
                 np.testing.assert_allclose(lb, lse, rtol=0, atol=1e-12)
             for bc in (1, 32, 13):

@@ -11,7 +11,12 @@ import attention_fa_fwd_02_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libfa.so not built")
+
+
+@pytest.fixture(autouse=True)
+def _library(libfa):
+    """Every test here needs the built library: a missing or broken build fails them."""
+    return libfa
 
 
 def declared_functions():
@@ -27,7 +32,7 @@ def test_exports_every_declared_symbol():
                           "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
                           "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args", "fa_bwd",
                           "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
-                          "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args"}
+                          "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_fwd_kernel_name"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -104,6 +109,16 @@ def test_grid_limit_depends_on_query_block():
     assert check(D=256, **big) == fa.FA_ERR_UNSUPPORTED
 
 
+def test_kernel_name():
+    """The dispatch's kernel, named as the profiler reports it; "" for sizes fa_fwd rejects."""
+    assert fa.fa_fwd_kernel_name(4, 16, 4096, 128, 0, 1, 256) == "fa_fwd_pp_kernel<Bf16, 128, false, 0>"
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 256, 1, 2, 256) == "fa_fwd_mfma_kernel<F16, 256, true, 0>"
+    assert fa.fa_fwd_kernel_name(1, 1, 128, 64, 0, 0, 256).startswith("fa_fwd_f32_kernel<64, false")
+    assert fa.fa_fwd_kernel_name(1, 1, 128, 48, 0, 1, 256) == ""
+    assert fa.fa_fwd_kernel_name(1, 1, 128, 64, 2, 1, 256) == ""
+    assert fa.fa_fwd_kernel_name(1, 1, 128, 64, 0, 1, 0) == ""
+
+
 def test_unsupported_arch():
     assert check(arch="gfx942:sramecc+:xnack-") == fa.FA_ERR_UNSUPPORTED
     assert check(arch="gfx1100") == fa.FA_ERR_UNSUPPORTED
@@ -115,6 +130,58 @@ def test_fwd_reports_invalid_args_before_any_hip_call():
     assert st == fa.FA_ERR_INVALID_ARG
     st = fa.fa_fwd(Q, K, V, O, L, 1, 1, 64, 48, 0.125, 0, 1, 0)
     assert st == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,H,N", [(1 << 35, 1 << 35, 1), (1 << 31, 1, 1), (1, 1 << 31, 1),
+                                    (1 << 30, 1 << 30, 1 << 10), ((1 << 62) + 1, 4, 1)])
+def test_size_products_do_not_wrap(B, H, N):
+    """B*H (and B*H*N) beyond the limits are refused even where the 64-bit
+    product would wrap to a small value (2^35 * 2^35 = 2^70 wraps to 0)."""
+    big = dict(q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T)
+    assert check(B=B, H=H, N=N, **big) == fa.FA_ERR_UNSUPPORTED
+    assert bcheck(B=B, H=H, N=N, q=T, k=2 * T, v=3 * T, o=4 * T, do=5 * T, lse=6 * T, dq=7 * T, dk=8 * T,
+                  dv=9 * T, ws=10 * T, wsb=1 << 62) == fa.FA_ERR_UNSUPPORTED
+    if N < (1 << 24):
+        assert f8check(B=B, H=H, N=N, wsb=1 << 62) == fa.FA_ERR_UNSUPPORTED
+
+
+class _FakeDeviceTensor:
+    """Duck-typed stand-in for a device tensor (no GPU here): only the
+    attributes the binding's output checks read."""
+
+    def __init__(self, shape, dtype, contiguous=True, device="cuda:0", is_cuda=True):
+        import torch
+        self.shape, self.dtype, self._c = tuple(shape), dtype, contiguous
+        self.device, self.is_cuda = torch.device(device), is_cuda
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_output_checks():
+    """Caller-supplied out= / lse= tensors must match exactly what the kernel
+    writes through their raw pointers."""
+    import torch
+    dev = torch.device("cuda:0")
+    ok = _FakeDeviceTensor((2, 3, 100, 64), torch.bfloat16)
+    fa._check_out(ok, "out", (2, 3, 100, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError):  # too small
+        fa._check_out(_FakeDeviceTensor((2, 3, 99, 64), torch.bfloat16), "out", (2, 3, 100, 64), torch.bfloat16, dev)
+    with pytest.raises(TypeError):  # wrong element size
+        fa._check_out(_FakeDeviceTensor((2, 3, 100, 64), torch.float32), "out", (2, 3, 100, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError):  # strided
+        fa._check_out(_FakeDeviceTensor((2, 3, 100, 64), torch.bfloat16, contiguous=False), "out",
+                      (2, 3, 100, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError):  # host memory
+        fa._check_out(_FakeDeviceTensor((2, 3, 100), torch.float32, device="cpu", is_cuda=False), "lse",
+                      (2, 3, 100), torch.float32, dev)
+    with pytest.raises(ValueError):  # another device
+        fa._check_out(_FakeDeviceTensor((2, 3, 100), torch.float32, device="cuda:1"), "lse",
+                      (2, 3, 100), torch.float32, dev)
+    # real host tensors are refused outright
+    x = torch.zeros(2, 3, 100, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa._check_out(x, "out", x.shape, x.dtype, dev)
 
 
 def test_python_wrapper_rejects_host_tensors():

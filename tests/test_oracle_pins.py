@@ -100,40 +100,21 @@ def test_planted_mistake_fails_some_pin(name, tmp_path):
     assert caught, "planted mistake %s passed every pin" % name
 
 
-@pytest.mark.parametrize("mutation", ["no_alpha", "alpha_sign", "per_block_softmax"])
-def test_broken_recurrence_disagrees_with_oracle(mutation):
+@pytest.mark.parametrize("mutation", ["no_rescale", "flipped_exponent", "block_softmax"])
+def test_broken_merge_disagrees_with_oracle(mutation):
     """The blocked recomputation is a sensitive check: dropping the exp(m_old - m_new)
-    rescale, flipping its sign, or normalising each key block separately and
-    concatenating (lesson 13 lists the last as a disqualifying misconception)
-    must all break agreement with the oracle."""
+    rescale when block statistics are combined, flipping its exponent, or
+    normalising each key block separately (lesson 13 lists "softmax each block and
+    concatenate" as a disqualifying misconception) must all break agreement with
+    the oracle."""
     rng = np.random.default_rng(21)
     n, d = 96, 16
     q, k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d)), rng.standard_normal((n, d))
     sc = 1.0 / math.sqrt(d)
     o, lse = oracle_attn(q, k, v, sc, False)
-    ob = np.zeros((n, d))
-    for r0 in range(0, n, 32):
-        rows = slice(r0, r0 + 32)
-        m = np.full(32, -np.inf)
-        l = np.zeros(32)
-        acc = np.zeros((32, d))
-        for c0 in range(0, n, 32):
-            s = sc * (q[rows] @ k[c0:c0 + 32].T)
-            if mutation == "per_block_softmax":
-                w = np.exp(s - s.max(axis=1, keepdims=True))
-                acc += (w / w.sum(axis=1, keepdims=True)) @ v[c0:c0 + 32]
-                l = np.ones(32)
-                continue
-            m_new = np.maximum(m, s.max(axis=1))
-            alpha = np.exp(m - m_new) if mutation != "alpha_sign" else np.exp(m_new - m)
-            alpha = np.where(np.isfinite(m), alpha, 0.0)
-            if mutation == "no_alpha":
-                alpha = np.where(np.isfinite(m), 1.0, 0.0)
-            w = np.exp(s - m_new[:, None])
-            l = l * alpha + w.sum(axis=1)
-            acc = acc * alpha[:, None] + w @ v[c0:c0 + 32]
-            m = m_new
-        ob[rows] = acc / l[:, None]
+    ok, _ = oc.blocked_tree(q, k, v, sc, False, 32, 32)
+    assert np.abs(ok - o).max() < 1e-12
+    ob, _ = oc.blocked_tree(q, k, v, sc, False, 32, 32, mutation=mutation)
     assert np.abs(ob - o).max() > 1e-3
 
 
@@ -149,7 +130,7 @@ def test_lesson13_seeded_example():
     k = rng.standard_normal((n, d)) * g["k_multiplier"]
     v = rng.standard_normal((n, d)) * g["v_multiplier"]
     o, lse = oracle_attn(q, k, v, g["scale"], False)
-    ob, lb = oc.blocked_online(q, k, v, g["scale"], False, g["block_size"], g["block_size"])
+    ob, lb = oc.blocked_tree(q, k, v, g["scale"], False, g["block_size"], g["block_size"])
     err = np.abs(o - ob).max()
     assert err < 1e-13, err
     assert err <= g["asserted_atol"]
