@@ -5,7 +5,7 @@ of the computation runs in the HIP kernels of ``libfa.so``; this module only
 marshals arguments.  There is no fallback: if the library is missing or the
 device is not gfx950 the calls raise.
 
-Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``,
+Names follow the C ABI: ``fa_fwd``, ``fa_check_args``, ``fa_fwd_split``, ``fa_fwd_split_static``,
 ``fa_fwd_split_workspace_bytes``, ``fa_fwd_split_choose``, ``fa_lse_merge``,
 ``fa_fwd_varlen``, ``fa_check_varlen_args``, ``fa_bwd``,
 ``fa_bwd_workspace_bytes``, ``fa_check_bwd_args``, ``fa_fwd_fp8``,
@@ -24,7 +24,8 @@ import os
 
 __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_MAX_SPLITS", "FaError", "lib_path",
-           "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
+           "load_library", "fa_fwd", "fa_check_args", "fa_fwd_split", "fa_fwd_split_static",
+           "fa_fwd_split_workspace_bytes", "FA_STATIC_SCRATCH_BYTES",
            "fa_fwd_split_choose", "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args",
            "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
            "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_fwd_kernel_name", "fa_status_string",
@@ -33,6 +34,7 @@ __all__ = ["FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FA_OK", "FA_ERR_INV
 FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_MAX_SPLITS = 64
+FA_STATIC_SCRATCH_BYTES = 64 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -67,6 +69,9 @@ def load_library():
         lib.fa_fwd_split.restype = ctypes.c_int
         lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
                                      ctypes.c_int, ctypes.c_int, i64, vp, ctypes.c_uint64, vp]
+        lib.fa_fwd_split_static.restype = ctypes.c_int
+        lib.fa_fwd_split_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                            ctypes.c_int, ctypes.c_int, i64, vp]
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_uint64
         lib.fa_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         lib.fa_fwd_split_choose.restype = i64
@@ -137,6 +142,14 @@ def fa_fwd_split(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: in
     """Raw C call with integer device addresses; returns the fa_status code."""
     return int(load_library().fa_fwd_split(q, k, v, o, lse, B, H, N, D, scale, causal, dtype,
                                            n_splits, workspace, workspace_bytes, stream))
+
+
+def fa_fwd_split_static(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, D: int,
+                        scale: float, causal: int, dtype: int, n_splits: int, stream: int) -> int:
+    """Raw C call (split partials in the library's static device array, no
+    workspace argument, no allocation); returns the fa_status code."""
+    return int(load_library().fa_fwd_split_static(q, k, v, o, lse, B, H, N, D, scale, causal, dtype,
+                                                  n_splits, stream))
 
 
 def fa_fwd_split_workspace_bytes(B: int, H: int, N: int, D: int, n_splits: int) -> int:

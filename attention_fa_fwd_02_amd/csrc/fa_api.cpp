@@ -89,6 +89,36 @@ bool prod_below(int64_t a, int64_t b, int64_t lim) { return a <= (lim - 1) / b; 
 
 } // namespace
 
+namespace fa {
+
+fa_status check_device_arch() { return check_device(); }
+
+fa_status split_grid_ok(int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_splits) {
+    const int64_t n_qblk = (N + query_block(D) - 1) / query_block(D);
+    if (B * H * n_qblk * n_splits >= (int64_t(1) << 23))
+        return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status split_enqueue(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                        int64_t N, int64_t D, float scale, int causal, fa_dtype dtype, int64_t n_splits,
+                        void *workspace, fa_stream_t stream) {
+    FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
+    const int64_t rows = B * H * N;
+    args.part_o = (float *)workspace;
+    args.part_lse = (float *)((char *)workspace + (uint64_t)n_splits * (uint64_t)rows * (uint64_t)D * 4u);
+    args.part_rows = rows;
+    args.split_keys = (int32_t)split_keys(N, n_splits);
+    args.n_splits = (int32_t)n_splits;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = launch_fwd((int)dtype, (int)D, causal != 0, kSplit, B * H * n_splits, args, hs);
+    if (err == hipSuccess)
+        err = launch_merge((int)dtype, args.part_o, args.part_lse, (int)n_splits, rows, (int)D, o, lse, hs);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+} // namespace fa
+
 extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -231,25 +261,11 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
         overlaps(workspace, need, v, tbytes) || overlaps(workspace, need, o, tbytes) ||
         overlaps(workspace, need, lse, lbytes))
         return FA_ERR_INVALID_ARG;
-    const int64_t n_qblk = (N + fa::query_block(D) - 1) / fa::query_block(D);
-    if (BH * n_qblk * n_splits >= (int64_t(1) << 23))
-        return FA_ERR_UNSUPPORTED;
+    if ((st = fa::split_grid_ok(B, H, N, D, n_splits)) != FA_OK)
+        return st;
     if ((st = check_device()) != FA_OK)
         return st;
-
-    fa::FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
-    const int64_t rows = BH * N;
-    args.part_o = (float *)workspace;
-    args.part_lse = (float *)((char *)workspace + (uint64_t)n_splits * (uint64_t)rows * (uint64_t)D * 4u);
-    args.part_rows = rows;
-    args.split_keys = (int32_t)split_keys(N, n_splits);
-    args.n_splits = (int32_t)n_splits;
-    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kSplit, BH * n_splits, args, hs);
-    if (err == hipSuccess)
-        err = fa::launch_merge((int)dtype, args.part_o, args.part_lse, (int)n_splits, rows, (int)D, o,
-                               lse, hs);
-    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+    return fa::split_enqueue(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, n_splits, workspace, stream);
 }
 
 fa_status fa_check_varlen_args(const void *q, const void *k, const void *v, const void *o,

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/fa.h"
+
 namespace fa {
 
 // Kernel arguments, passed by value.
@@ -94,6 +96,17 @@ struct BwdArgs {
 // problem; arguments are already validated.
 hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &args,
                       hipStream_t stream);
+
+// Host-side pieces of the key-split path shared by fa_fwd_split and its
+// static-scratch variant (arguments already validated by the caller):
+// the current device is gfx950; the split grid fits one launch; enqueue the
+// split kernel and the merge with the partials in `workspace`
+// (fa_fwd_split_workspace_bytes bytes, 16-byte aligned).
+fa_status check_device_arch();
+fa_status split_grid_ok(int64_t B, int64_t H, int64_t N, int64_t D, int64_t n_splits);
+fa_status split_enqueue(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                        int64_t N, int64_t D, float scale, int causal, fa_dtype dtype, int64_t n_splits,
+                        void *workspace, fa_stream_t stream);
 
 // Merge n_parts partial results per row: part_o [n_parts][rows][D] fp32,
 // part_lse [n_parts][rows]; writes o [rows][D] (dtype 0 fp32, 1 bf16, 2 fp16)

@@ -175,6 +175,35 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o, flo
                        fa_stream_t stream);
 
 /*
+ * fa_fwd_split_static -- fa_fwd_split without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The split partials
+ * go to a device array the library holds: FA_STATIC_SCRATCH_BYTES bytes per
+ * device, allocated when the library's code object is loaded onto a device
+ * and kept until the process ends (not by this call).  The call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ *   arguments  as for fa_fwd_split, minus workspace / workspace_bytes.
+ *
+ * Every call on one device uses that device's same array, which keeps the
+ * last call's partials: calls that overlap on one device (concurrent
+ * streams, or other host threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero.
+ *
+ * Errors: the checks of fa_fwd_split, except FA_ERR_UNSUPPORTED (not
+ * FA_ERR_INVALID_ARG) when fa_fwd_split_workspace_bytes(B, H, N, D,
+ * n_splits) exceeds FA_STATIC_SCRATCH_BYTES; FA_ERR_HIP if the array's device
+ * address cannot be looked up or a launch fails.  All argument checks precede
+ * any HIP call.  Results are bitwise those of fa_fwd_split with the same
+ * n_splits.
+ */
+#define FA_STATIC_SCRATCH_BYTES (64u << 20)
+
+fa_status fa_fwd_split_static(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                              fa_dtype dtype, int64_t n_splits, fa_stream_t stream);
+
+/*
  * fa_lse_merge -- merge n_parts partial results per row (formula above).
  *
  *   part_o    device pointer, fp32 [n_parts][rows][D], 16-byte aligned; part

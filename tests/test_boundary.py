@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                           "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_choose",
                           "fa_lse_merge", "fa_fwd_varlen", "fa_check_varlen_args", "fa_bwd",
                           "fa_bwd_workspace_bytes", "fa_check_bwd_args", "fa_fwd_fp8",
-                          "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_fwd_kernel_name"}
+                          "fa_fwd_fp8_workspace_bytes", "fa_check_fp8_args", "fa_fwd_kernel_name",
+                          "fa_fwd_split_static"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -198,6 +199,28 @@ def test_python_wrapper_rejects_host_tensors():
 def test_max_splits_matches_header():
     m = re.search(r"#define FA_MAX_SPLITS (\d+)", open(HEADER).read())
     assert fa.FA_MAX_SPLITS == int(m.group(1))
+
+
+def test_static_scratch_size_matches_header():
+    m = re.search(r"#define FA_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert fa.FA_STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
+def test_split_static_checks_before_any_hip_call():
+    """Argument errors and sizes beyond the static array are reported on the host
+    (safe without a GPU: no HIP call is reached)."""
+    f = fa.fa_fwd_split_static
+    assert f(0, K, V, O, L, 1, 1, 64, 64, 0.125, 0, 1, 2, 0) == fa.FA_ERR_INVALID_ARG
+    assert f(Q, K, V, O, L, 1, 1, 64, 64, float("nan"), 0, 1, 2, 0) == fa.FA_ERR_INVALID_ARG
+    assert f(Q, K, V, O, L, 1, 1, 64, 64, 0.125, 0, 1, 0, 0) == fa.FA_ERR_INVALID_ARG
+    assert f(Q, K, V, O, L, 1, 1, 64, 48, 0.125, 0, 1, 2, 0) == fa.FA_ERR_UNSUPPORTED
+    assert f(Q, K, V, O, L, 1, 1, 64, 64, 0.125, 0, 1, fa.FA_MAX_SPLITS + 1, 0) == fa.FA_ERR_UNSUPPORTED
+    # partials of B1 H2 N8192 D128 in 16 splits: 16*2*8192*129*4 bytes > 64 MiB
+    big = dict(q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T)
+    need = fa.fa_fwd_split_workspace_bytes(1, 2, 8192, 128, 16)
+    assert need > fa.FA_STATIC_SCRATCH_BYTES
+    assert f(big["q"], big["k"], big["v"], big["o"], big["lse"], 1, 2, 8192, 128, 0.1, 0, 1, 16, 0) \
+        == fa.FA_ERR_UNSUPPORTED
 
 
 def test_split_workspace_bytes():
