@@ -14,6 +14,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::once_flag g_arch_once[kMaxDevices];
 char g_arch[kMaxDevices][256];
+int g_cus[kMaxDevices];
 hipError_t g_arch_err[kMaxDevices];
 
 size_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
@@ -31,8 +32,9 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
-// Current device must be gfx950 (cached per device after the first query).
-fa_status check_device() {
+// Current device must be gfx950 (cached per device after the first query,
+// with its compute-unit count, stored in *n_cus when asked for).
+fa_status check_device(int *n_cus = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return FA_ERR_HIP;
@@ -42,12 +44,15 @@ fa_status check_device() {
         if (g_arch_err[dev] == hipSuccess) {
             std::strncpy(g_arch[dev], prop.gcnArchName, sizeof(g_arch[dev]) - 1);
             g_arch[dev][sizeof(g_arch[dev]) - 1] = '\0';
+            g_cus[dev] = prop.multiProcessorCount;
         }
     });
     if (g_arch_err[dev] != hipSuccess)
         return FA_ERR_HIP;
     if (std::strncmp(g_arch[dev], "gfx950", 6) != 0)
         return FA_ERR_UNSUPPORTED;
+    if (n_cus)
+        *n_cus = g_cus[dev];
     return FA_OK;
 }
 
@@ -152,7 +157,8 @@ const char *fa_fwd_kernel_name(int64_t B, int64_t H, int64_t N, int64_t D, int c
     float *lse = (float *)(base + 4 * step);
     if (n_cus < 1 || fa_check_args(q, k, v, o, lse, B, H, N, D, 0.f, causal, dtype, nullptr) != FA_OK)
         return "";
-    return fa::fwd_kernel_name(dtype, (int)D, causal != 0, fa::kDense);
+    return fa::fwd_kernel_name(dtype, (int)D, causal != 0, fa::kDense,
+                               fa::choose_key_groups(B * H, N, D, dtype, n_cus));
 }
 
 fa_status fa_check_args(const void *q, const void *k, const void *v, const void *o,
@@ -204,11 +210,15 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     fa_status st = fa_check_args(q, k, v, o, lse, B, H, N, D, scale, causal, (int)dtype, nullptr);
     if (st != FA_OK)
         return st;
-    if ((st = check_device()) != FA_OK)
+    int n_cus = 0;
+    if ((st = check_device(&n_cus)) != FA_OK)
         return st;
-    const fa::FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
+    fa::FwdArgs args = make_args(q, k, v, o, lse, N, D, scale, dtype);
+    const int kg = fa::choose_key_groups(B * H, N, D, (int)dtype, n_cus);
+    const int64_t qblk = fa::query_block(D) / kg;
+    args.n_qblk = (int32_t)((N + qblk - 1) / qblk);
     const hipError_t err = fa::launch_fwd((int)dtype, (int)D, causal != 0, fa::kDense, B * H, args,
-                                          reinterpret_cast<hipStream_t>(stream));
+                                          reinterpret_cast<hipStream_t>(stream), kg);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

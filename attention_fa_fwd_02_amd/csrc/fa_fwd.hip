@@ -377,10 +377,10 @@ struct SliceBlock {
     int q0, q0w;   // first query row of the block / of this wave
     int k_begin, kv_end, n_tiles;
 };
-template <int D, int MODE, bool CAUSAL>
+template <int D, int MODE, bool CAUSAL, int KG = 1>
 __device__ __forceinline__ SliceBlock slice_block(const FwdArgs &a, int wave) {
     static_assert(MODE == kDense || MODE == kSplit, "square slices");
-    constexpr int QBLK = MfmaCfg<D>::QBLK, BC = MfmaCfg<D>::BC;
+    constexpr int QBLK = MfmaCfg<D>::QBLK / KG, BC = MfmaCfg<D>::BC;
     constexpr bool SPLIT = MODE == kSplit;
     const Work wk = map_workgroup(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
     SliceBlock k;
@@ -388,7 +388,7 @@ __device__ __forceinline__ SliceBlock slice_block(const FwdArgs &a, int wave) {
     k.bh = SPLIT ? wk.bh / a.n_splits : wk.bh;
     k.split = SPLIT ? wk.bh - k.bh * a.n_splits : 0;
     k.q0 = wk.qb * QBLK;
-    k.q0w = k.q0 + 32 * wave;
+    k.q0w = k.q0 + 32 * (wave / KG); // with key groups, waves kg*r .. kg*r + kg-1 share rows
     k.k_begin = SPLIT ? k.split * a.split_keys : 0;
     const int kv_vis = CAUSAL ? min(a.N, k.q0 + QBLK) : a.N;
     k.kv_end = SPLIT ? min(kv_vis, k.k_begin + a.split_keys) : kv_vis;
@@ -672,14 +672,26 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 // 2t + 1 and V(t) in phases 2t + 2 and 2t + 3, so two K stages and two V
 // stages (separate LDS objects, so the loads into one are never waited for
 // before reads of another) hold every tile for as long as it is read.
-template <typename E, int D, bool CAUSAL, int MODE>
+//
+// Key groups (KG = 2 or 4, whole slices only), for grids too small to fill the
+// device: the workgroup takes 256 / KG query rows, and wave w takes the rows
+// of row group w / KG and the keys of key group w % KG, i.e. keys
+// [(w % KG) * 128 / KG, ...) of every tile.  Waves w and w + 4 still share a
+// key group and so step through the same sub-tiles half a tile apart.  At the
+// end each wave's unnormalised (m, l, O) goes to LDS and the KG partials of
+// every row are combined with the same exp(m_k - m) rescale as across key
+// tiles before O / l is rounded and stored.
+template <typename E, int D, bool CAUSAL, int MODE, int KG>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit;
     using Cfg = MfmaCfg<D>;
     static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
     static_assert(MODE != kVarlen, "square [B, H, N, D] slices only");
+    static_assert(KG == 1 || ((KG == 2 || KG == 4) && MODE == kDense), "key groups of whole slices");
     constexpr int W = Cfg::WAVES, BC = Cfg::BC;
-    constexpr int KB = BC / 32, DC = D / 16, OB = D / 32;
+    constexpr int BCS = BC / KG;         // keys of a wave's share of a tile
+    constexpr int QBLK = Cfg::QBLK / KG; // query rows of the workgroup
+    constexpr int KB = BCS / 32, DC = D / 16, OB = D / 32;
     constexpr int KP = Cfg::KP, VP = Cfg::VP, OP = Cfg::OP;
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
     constexpr int KBYTES = NK * 1024;               // K stage: the K tile
@@ -702,9 +714,10 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int g = lane >> 5;
 
     // --- slice, query block, key range ----------------------------------------
-    const SliceBlock blk = slice_block<D, MODE, CAUSAL>(a, wave);
+    const SliceBlock blk = slice_block<D, MODE, CAUSAL, KG>(a, wave);
     if (split_block_empty<D, MODE>(blk, a, tid))
         return;
+    const int kws = (wave % KG) * BCS; // the wave's keys inside a tile
     const int N = a.N;
     const int64_t off = (int64_t)blk.bh * N * D;
     const uint16_t *__restrict__ Q = (const uint16_t *)a.q + off;
@@ -761,12 +774,19 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     uint32_t pk[KB][8]; // its weights, rounded, as the PV operand
 
     // a tile is skipped by a wave none of whose rows sees any of its keys
+    // (written separately for whole-tile waves: stated through kws the dense
+    // causal instances spill)
     auto active = [&](int t) __attribute__((always_inline)) {
-        return (q0w < N) && (!CAUSAL || k_begin + t * BC <= q0w + 31);
+        if constexpr (KG == 1) {
+            return (q0w < N) && (!CAUSAL || k_begin + t * BC <= q0w + 31);
+        } else {
+            const int k0 = k_begin + t * BC + kws;
+            return (q0w < N) && (k0 < kv_end) && (!CAUSAL || k0 <= q0w + 31);
+        }
     };
     // S^T = K Q^T : s[kb][i] = score(query qi, key k0 + 32kb + 2i + g)
     auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
-        const lds_char *ks = kst + k_lane;
+        const lds_char *ks = kst + k_lane + kws * KP;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             s[kb] = f32x16{};
@@ -790,7 +810,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     // query qi.  Consecutive MFMAs go to different accumulators; each o[b]
     // still adds its (kb, mm) terms in order.
     auto accumulate = [&](const lds_char *vst) __attribute__((always_inline)) {
-        const lds_char *vs = vst + v_lane;
+        const lds_char *vs = vst + v_lane + kws * VP;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -818,9 +838,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int k0 = k_begin + t * BC;
+        const int k0 = k_begin + t * BC + kws;
         // masking: keys beyond N, and keys after the query when causal
-        if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w))
+        if ((k0 + BCS > N) || (CAUSAL && k0 + BCS - 1 > q0w))
             mask_keys<KB, CAUSAL>(s, k0, N, qi, 0, g);
         online_softmax<E, KB, OB>(s, pk, o, m_run, l_run, c);
     };
@@ -885,6 +905,60 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int sa = wave >> 1;
     lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
     const float l_tot = pair_sum(l_run);
+    if constexpr (KG > 1) {
+        // each wave's unnormalised O (fp32, wave-private rows at pitch 4D + 16
+        // bytes in the stage arrays) and its rows' (m, l)
+        constexpr int OP4 = 4 * D + 16;
+        static_assert(2 * 32 * OP4 <= KBYTES, "two waves' fp32 O rows fit in a stage array");
+        __shared__ float ml[W][2][32];
+        lds_char *const ow = own + (wave & 1) * 32 * OP4;
+#pragma unroll
+        for (int b = 0; b < OB; ++b)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const f32x4 w4 = {o[b][4 * a4], o[b][4 * a4 + 1], o[b][4 * a4 + 2], o[b][4 * a4 + 3]};
+                *(__attribute__((address_space(3))) f32x4 *)(ow + r * OP4 + (32 * b + 8 * a4 + 4 * g) * 4) = w4;
+            }
+        if (g == 0) {
+            ml[wave][0][r] = m_run;
+            ml[wave][1][r] = l_tot;
+        }
+        __syncthreads();
+        // combine the KG partials of each row: m = max m_k, O = sum e^(m_k - m) O_k,
+        // l = sum e^(m_k - m) l_k (exp2 domain); one 16-byte chunk of a row per item
+        constexpr int CH = D / 8, ITEMS = QBLK * CH;
+        for (int it = tid; it < ITEMS; it += W * 64) {
+            const int row = it / CH, ch = it - (it / CH) * CH;
+            const int w0 = (row >> 5) * KG, rr = row & 31;
+            float m = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < KG; ++kk)
+                m = fmaxf(m, ml[w0 + kk][0][rr]);
+            float lsum = 0.f;
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KG; ++kk) {
+                const int wk = w0 + kk, sk = wk >> 1;
+                const float mk = ml[wk][0][rr];
+                const float f = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - m);
+                lsum += f * ml[wk][1][rr];
+                const lds_char *base = sk == 0 ? ks0 : sk == 1 ? ks1 : sk == 2 ? vs0 : vs1;
+                const lds_char *p = base + (wk & 1) * 32 * OP4 + rr * OP4 + ch * 32;
+                acc0 += f * *(const __attribute__((address_space(3))) f32x4 *)p;
+                acc1 += f * *(const __attribute__((address_space(3))) f32x4 *)(p + 16);
+            }
+            const int q = blk.q0 + row;
+            if (q < N) {
+                const float inv = 1.0f / lsum;
+                const u32x4 w4 = {E::pack(acc0[0] * inv, acc0[1] * inv), E::pack(acc0[2] * inv, acc0[3] * inv),
+                                  E::pack(acc1[0] * inv, acc1[1] * inv), E::pack(acc1[2] * inv, acc1[3] * inv)};
+                *(u32x4 *)(O + (int64_t)q * D + ch * 8) = w4;
+                if (ch == 0)
+                    LSE[q] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
+            }
+        }
+        return;
+    }
     if constexpr (SPLIT) {
         constexpr int OP4 = 4 * D + 16; // fp32 staging row pitch (bytes)
         static_assert(2 * 32 * OP4 <= KBYTES, "two waves' fp32 O rows fit in a stage array");
@@ -900,25 +974,32 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
 // ----------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2_f32)
 // ----------------------------------------------------------------------------
-template <int D>
+// KG key groups (dense launches of small grids): a stage holds KG tiles of 32
+// keys, wave w takes rows of row group w / KG and the tile w % KG of every
+// stage, and the workgroup covers 256 / KG query rows (as in the 16-bit
+// kernel; its partials are combined the same way at the end).
+template <int D, int KG = 1>
 struct F32Cfg {
-    static constexpr int BC = 32;
+    static constexpr int BC = 32 * KG; // keys per stage
     static constexpr int KP = D + 1; // padded K row (floats): column reads hit 32 banks
     static constexpr int KSTAGE = BC * KP * 4;
     static constexpr int STAGE = KSTAGE + BC * D * 4;
     static constexpr int LDS = 2 * STAGE;
+    static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
 };
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, int KG>
 __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
-    using Cfg = F32Cfg<D>;
+    static_assert(KG == 1 || ((KG == 2 || KG == 4) && MODE == kDense), "key groups of whole slices");
+    using Cfg = F32Cfg<D, KG>;
     constexpr int BC = Cfg::BC;
     constexpr int KP = Cfg::KP;
+    constexpr int QBLK = kQueryBlock / KG;  // query rows of the workgroup
     constexpr int H2 = D / 2;               // k-steps of the score MFMA
     constexpr int OB = D / 32;
     constexpr int C4 = D / 4;               // 16-byte chunks per row
-    constexpr int NCH = BC * C4 / kThreads; // chunks per thread per tile (1 or 2)
+    constexpr int NCH = BC * C4 / kThreads; // chunks per thread per stage
     static_assert(NCH * kThreads == BC * C4, "tile chunks divide evenly");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -960,18 +1041,19 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
     float *__restrict__ LSE = SPLIT ? a.part_lse + split * a.part_rows + (int64_t)bh * a.N
                                     : a.lse + lse_off;
 
-    const int q0 = wk.qb * kQueryBlock;
-    const int q0w = q0 + 32 * wave;
+    const int q0 = wk.qb * QBLK;
+    const int q0w = q0 + 32 * (wave / KG);
     const int qi = q0w + r;
+    const int kws = 32 * (wave % KG); // the wave's 32 keys inside a stage
     if (VARLEN && q0 >= Nq) // the grid covers the longest sequence
         return;
     const int k_begin = SPLIT ? split * a.split_keys : 0;
-    const int kv_vis = CAUSAL ? min(Nk, q0 + kQueryBlock + coff) : Nk;
+    const int kv_vis = CAUSAL ? min(Nk, q0 + QBLK + coff) : Nk;
     const int kv_end = SPLIT ? min(kv_vis, k_begin + a.split_keys) : kv_vis;
     const int n_tiles = (SPLIT || VARLEN) ? (kv_end > k_begin ? (kv_end - k_begin + BC - 1) / BC : 0)
                                           : (kv_end + BC - 1) / BC;
     if ((SPLIT || VARLEN) && n_tiles == 0) { // no key is visible to any row of the block
-        if (tid < kQueryBlock && q0 + tid < Nq) {
+        if (tid < QBLK && q0 + tid < Nq) {
             if (VARLEN) { // O = 0 (a split leaves an empty partial's O unwritten)
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1042,18 +1124,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         const int stage = t & 1;
         if (t + 1 < n_tiles)
             load_tile(t + 1);
-        const int k0 = k_begin + t * BC;
-        const bool active = (q0w < Nq) && (!CAUSAL || k0 <= q0w + 31 + coff);
+        const int k0 = k_begin + t * BC + kws;
+        const bool active = (q0w < Nq) && (KG == 1 || k0 < kv_end) && (!CAUSAL || k0 <= q0w + 31 + coff);
         if (active) {
-            const float *ks = (const float *)(smem + stage * Cfg::STAGE);
-            const float *vs = (const float *)(smem + stage * Cfg::STAGE + Cfg::KSTAGE);
+            const float *ks = (const float *)(smem + stage * Cfg::STAGE) + kws * KP;
+            const float *vs = (const float *)(smem + stage * Cfg::STAGE + Cfg::KSTAGE) + kws * D;
             // s[i] = score(query qi, key k0 + 16g + i)
             f32x16 s = f32x16{};
             const float *krow = ks + row_perm(r) * KP + H2 * g;
 #pragma unroll
             for (int j = 0; j < H2; ++j)
                 s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[j], qf[j], s, 0, 0, 0);
-            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff);
+            const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > q0w + coff);
             if (need_mask) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -1096,6 +1178,76 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdArgs a) {
         __syncthreads();
     }
 
+    if constexpr (KG > 1) {
+        // the waves of key groups 1 .. KG-1 publish their unnormalised O and (m, l)
+        // in LDS (the tile stages are free: the loop ended with a barrier after
+        // the last tile's reads); the group-0 wave of each row group adds them
+        // to its own with the exp(m_k - m) rescale and stores the rows
+        constexpr int OP = D + 4;           // fp32 row pitch of a published O (floats)
+        constexpr int NS = kWaves - kWaves / KG; // publishing waves
+        static_assert(NS * 32 * OP * 4 + NS * 64 * 4 <= Cfg::LDS, "partials fit the stages");
+        const int ksg = wave % KG, slot0 = (wave / KG) * (KG - 1) - 1; // slot of group k: slot0 + k
+        float *pml = (float *)smem + NS * 32 * OP;
+        const float l_tot = pair_sum(l_run);
+        if (ksg > 0) {
+            float *po = (float *)smem + (slot0 + ksg) * 32 * OP;
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 x = {o[b][4 * j], o[b][4 * j + 1], o[b][4 * j + 2], o[b][4 * j + 3]};
+                    *(f32x4 *)(po + r * OP + 32 * b + 16 * g + 4 * j) = x;
+                }
+            if (g == 0) {
+                pml[(slot0 + ksg) * 64 + r] = m_run;
+                pml[(slot0 + ksg) * 64 + 32 + r] = l_tot;
+            }
+        }
+        __syncthreads();
+        if (ksg == 0 && q0w < Nq) {
+            float m = m_run;
+#pragma unroll
+            for (int kk = 1; kk < KG; ++kk)
+                m = fmaxf(m, pml[(slot0 + kk) * 64 + r]);
+            // group 0 sees key 0 of the slice, so m is finite for every row
+            const float f0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+            float lsum = f0 * l_tot;
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+                o[b] *= f0;
+#pragma unroll
+            for (int kk = 1; kk < KG; ++kk) {
+                const float mk = pml[(slot0 + kk) * 64 + r];
+                const float f = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - m);
+                lsum += f * pml[(slot0 + kk) * 64 + 32 + r];
+                const float *po = (const float *)smem + (slot0 + kk) * 32 * OP + r * OP + 16 * g;
+#pragma unroll
+                for (int b = 0; b < OB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 x = *(const f32x4 *)(po + 32 * b + 4 * j);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            o[b][4 * j + e] += f * x[e];
+                    }
+            }
+            if (qi < Nq) {
+                const float inv = 1.0f / lsum;
+                float *orow = O + (int64_t)qi * D + 16 * g;
+#pragma unroll
+                for (int b = 0; b < OB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 x = {o[b][4 * j] * inv, o[b][4 * j + 1] * inv, o[b][4 * j + 2] * inv,
+                                         o[b][4 * j + 3] * inv};
+                        *(f32x4 *)(orow + 32 * b + 4 * j) = x;
+                    }
+                if (g == 0)
+                    LSE[qi] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
+            }
+        }
+        return;
+    }
     if (q0w < Nq) {
         const float l_tot = pair_sum(l_run);
         // a row that sees no key (split or packed sequence): l = 0, m = -inf -> O = 0, lse = -inf
@@ -1142,19 +1294,44 @@ hipError_t launch(int64_t nwg, int lds, const FwdArgs &args, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, int KG = 1>
 hipError_t launch_f32(int64_t nwg, const FwdArgs &args, hipStream_t stream) {
-    return launch<fa_fwd_f32_kernel<D, CAUSAL, MODE>>(nwg, F32Cfg<D>::LDS, args, stream);
+    return launch<fa_fwd_f32_kernel<D, CAUSAL, MODE, KG>>(nwg, F32Cfg<D, KG>::LDS, args, stream);
+}
+
+// key groups of the fp32 kernel: D = 64 only (at D = 128 the register-staged
+// loads of two 32-key tiles per stage do not fit without spilling)
+template <int D, bool CAUSAL, int MODE>
+hipError_t launch_f32_kg(int64_t nwg, const FwdArgs &args, hipStream_t stream, int kg) {
+    if constexpr (MODE == kDense && D == 64) {
+        if (kg == 4)
+            return launch_f32<D, CAUSAL, MODE, 4>(nwg, args, stream);
+        if (kg == 2)
+            return launch_f32<D, CAUSAL, MODE, 2>(nwg, args, stream);
+    }
+    return launch_f32<D, CAUSAL, MODE, 1>(nwg, args, stream);
+}
+
+template <typename E, int D, int MODE, int KG>
+hipError_t launch_pp(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
+    constexpr int T = MfmaCfg<D>::THREADS;
+    if (causal)
+        return launch<fa_fwd_pp_kernel<E, D, true, MODE, KG>, T>(nwg, 0, args, stream);
+    return launch<fa_fwd_pp_kernel<E, D, false, MODE, KG>, T>(nwg, 0, args, stream);
 }
 
 template <typename E, int D, int MODE>
-hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
+hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream, int kg) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     constexpr int T = MfmaCfg<D>::THREADS;
     if constexpr (MODE != kVarlen && MfmaCfg<D>::PINGPONG) {
-        if (causal)
-            return launch<fa_fwd_pp_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
-        return launch<fa_fwd_pp_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
+        if constexpr (MODE == kDense) {
+            if (kg == 4)
+                return launch_pp<E, D, MODE, 4>(causal, nwg, args, stream);
+            if (kg == 2)
+                return launch_pp<E, D, MODE, 2>(causal, nwg, args, stream);
+        }
+        return launch_pp<E, D, MODE, 1>(causal, nwg, args, stream);
     } else {
         if (causal)
             return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
@@ -1164,77 +1341,106 @@ hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_
 
 // head dims of the 16-bit kernels
 template <typename E, int MODE>
-hipError_t launch_mfma_d(int D, bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream) {
+hipError_t launch_mfma_d(int D, bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream, int kg) {
     switch (D) {
     case 64:
-        return launch_mfma<E, 64, MODE>(causal, nwg, args, stream);
+        return launch_mfma<E, 64, MODE>(causal, nwg, args, stream, kg);
     case 96:
-        return launch_mfma<E, 96, MODE>(causal, nwg, args, stream);
+        return launch_mfma<E, 96, MODE>(causal, nwg, args, stream, kg);
     case 128:
-        return launch_mfma<E, 128, MODE>(causal, nwg, args, stream);
+        return launch_mfma<E, 128, MODE>(causal, nwg, args, stream, kg);
     case 192:
-        return launch_mfma<E, 192, MODE>(causal, nwg, args, stream);
+        return launch_mfma<E, 192, MODE>(causal, nwg, args, stream, kg);
     default:
-        return launch_mfma<E, 256, MODE>(causal, nwg, args, stream);
+        return launch_mfma<E, 256, MODE>(causal, nwg, args, stream, kg);
     }
 }
 
 template <int MODE>
 hipError_t launch_dtype(int dtype, int D, bool causal, int64_t nwg, const FwdArgs &args,
-                        hipStream_t stream) {
+                        hipStream_t stream, int kg) {
     if (dtype == 0) {
         if (D == 64)
-            return causal ? launch_f32<64, true, MODE>(nwg, args, stream)
-                          : launch_f32<64, false, MODE>(nwg, args, stream);
-        return causal ? launch_f32<128, true, MODE>(nwg, args, stream)
-                      : launch_f32<128, false, MODE>(nwg, args, stream);
+            return causal ? launch_f32_kg<64, true, MODE>(nwg, args, stream, kg)
+                          : launch_f32_kg<64, false, MODE>(nwg, args, stream, kg);
+        return causal ? launch_f32_kg<128, true, MODE>(nwg, args, stream, kg)
+                      : launch_f32_kg<128, false, MODE>(nwg, args, stream, kg);
     }
     if (dtype == 1)
-        return launch_mfma_d<Bf16, MODE>(D, causal, nwg, args, stream);
-    return launch_mfma_d<F16, MODE>(D, causal, nwg, args, stream);
+        return launch_mfma_d<Bf16, MODE>(D, causal, nwg, args, stream, kg);
+    return launch_mfma_d<F16, MODE>(D, causal, nwg, args, stream, kg);
 }
 
 } // namespace
 
-const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode) {
-    // every (dtype, head dim, causal, mode) the dispatch below can reach, named
-    // as the profiler demangles the template instance
-    static char names[3][5][2][3][96];
+int choose_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, int64_t n_cus) {
+    // (the fp32 kernel takes key groups at D = 64 only)
+    if (D > 128 || n_cus < 1 || (dtype == 0 && D != 64))
+        return 1;
+    const int max_kg = 4;
+    const int64_t wg1 = BH * ((N + 255) / 256);
+    // relative efficiency of a workgroup with kg key groups (shorter phases per
+    // barrier, plus the combining epilogue)
+    const double eff[3] = {1.0, 0.9, 0.75};
+    int best = 1;
+    // rounds of workgroups per compute unit x work per workgroup
+    double best_t = (double)((wg1 + n_cus - 1) / n_cus);
+    for (int kg = 2, gi = 1; kg <= max_kg; kg *= 2, ++gi) {
+        const int64_t wg = BH * ((N + 256 / kg - 1) / (256 / kg));
+        const double t = (double)((wg + n_cus - 1) / n_cus) / kg / eff[gi];
+        if (t < best_t - 1e-9) {
+            best_t = t;
+            best = kg;
+        }
+    }
+    return best;
+}
+
+const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg) {
+    // every (dtype, head dim, causal, mode, key groups) the dispatch below can
+    // reach, named as the profiler demangles the template instance
+    static char names[3][5][2][3][3][96];
     static std::once_flag once;
     static const int dims[5] = {64, 96, 128, 192, 256};
     std::call_once(once, [] {
         for (int t = 0; t < 3; ++t)
             for (int di = 0; di < 5; ++di)
                 for (int c = 0; c < 2; ++c)
-                    for (int m = 0; m < 3; ++m) {
-                        const int d = dims[di];
-                        const char *cs = c ? "true" : "false";
-                        if (t == 0)
-                            snprintf(names[t][di][c][m], 96, "fa_fwd_f32_kernel<%d, %s, %d>", d, cs, m);
-                        else
-                            snprintf(names[t][di][c][m], 96, "%s<%s, %d, %s, %d>",
-                                     (m != kVarlen && d <= 128) ? "fa_fwd_pp_kernel" : "fa_fwd_mfma_kernel",
-                                     t == 1 ? "Bf16" : "F16", d, cs, m);
-                    }
+                    for (int m = 0; m < 3; ++m)
+                        for (int gi = 0; gi < 3; ++gi) {
+                            const int d = dims[di], g = 1 << gi;
+                            const char *cs = c ? "true" : "false";
+                            const char *e = t == 1 ? "Bf16" : "F16";
+                            char *out = names[t][di][c][m][gi];
+                            if (t == 0)
+                                snprintf(out, 96, "fa_fwd_f32_kernel<%d, %s, %d, %d>", d, cs, m,
+                                         m == kDense ? g : 1);
+                            else if (m != kVarlen && d <= 128)
+                                snprintf(out, 96, "fa_fwd_pp_kernel<%s, %d, %s, %d, %d>", e, d, cs, m,
+                                         m == kDense ? g : 1);
+                            else
+                                snprintf(out, 96, "fa_fwd_mfma_kernel<%s, %d, %s, %d>", e, d, cs, m);
+                        }
     });
     int di = -1;
     for (int i = 0; i < 5; ++i)
         if (dims[i] == D)
             di = i;
+    const int gi = kg == 4 ? 2 : kg == 2 ? 1 : 0;
     if (dtype < 0 || dtype > 2 || di < 0 || (int)mode < 0 || (int)mode > 2)
         return "";
-    return names[dtype][di][causal ? 1 : 0][(int)mode];
+    return names[dtype][di][causal ? 1 : 0][(int)mode][gi];
 }
 
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
-                      const FwdArgs &args, hipStream_t stream) {
+                      const FwdArgs &args, hipStream_t stream, int kg) {
     // one workgroup per (grid row, query block)
     const int64_t nwg = rows * (int64_t)args.n_qblk;
     if (mode == kSplit)
-        return launch_dtype<kSplit>(dtype, D, causal, nwg, args, stream);
+        return launch_dtype<kSplit>(dtype, D, causal, nwg, args, stream, 1);
     if (mode == kVarlen)
-        return launch_dtype<kVarlen>(dtype, D, causal, nwg, args, stream);
-    return launch_dtype<kDense>(dtype, D, causal, nwg, args, stream);
+        return launch_dtype<kVarlen>(dtype, D, causal, nwg, args, stream, 1);
+    return launch_dtype<kDense>(dtype, D, causal, nwg, args, stream, kg);
 }
 
 } // namespace fa

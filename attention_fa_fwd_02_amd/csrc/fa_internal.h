@@ -46,16 +46,26 @@ enum FwdMode { kDense = 0, kSplit = 1, kVarlen = 2 };
 constexpr int kQueryBlock = 256;
 constexpr int query_block(int64_t D) { return D > 192 ? 128 : 256; }
 
+// Key groups of a dense fa_fwd launch (1, 2 or 4): with kg > 1 the kernel
+// (16-bit for D <= 128, fp32 for D = 64) splits its 8 waves into 8/kg row
+// groups of 32 query rows times kg groups of keys, so a workgroup covers
+// query_block(D) / kg rows and the grid has kg times as many workgroups.  Chosen for grids of
+// B*H*ceil(N/256) workgroups that leave compute units idle: the kg that
+// minimises the number of rounds of workgroups per compute unit times the
+// work of one workgroup (ties go to the smaller kg).  Always 1 for D > 128
+// and for fp32 at D = 128.
+int choose_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, int64_t n_cus);
+
 // Enqueue the forward pass; arguments are already validated.  `rows` is the
 // number of grid rows: B*H slices (kDense), B*H*n_splits (kSplit, which
 // writes part_o / part_lse instead of o / lse) or n_seqs*n_heads (kVarlen);
 // each row has args.n_qblk query blocks.
 hipError_t launch_fwd(int dtype, int D, bool causal, FwdMode mode, int64_t rows,
-                      const FwdArgs &args, hipStream_t stream);
+                      const FwdArgs &args, hipStream_t stream, int kg = 1);
 
 // Name of the kernel launch_fwd runs for these arguments (static string; ""
 // for a combination it cannot launch).
-const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode);
+const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg = 1);
 
 // FP8 (E4M3) forward arguments, passed by value.
 struct Fp8Args {

@@ -236,21 +236,28 @@ def bench_one(name, steps, warmup, copy_calibration=False, flush=False, warm_sec
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # the timed steps: exactly `steps` calls back to back between two events
+    # (the throughput; per-call events would add host work between the calls)
     torch.cuda.synchronize()
-    # cold-cache variant: a 1 GiB fill between calls evicts the inputs from L2 and
-    # the 256 MB Infinity Cache; only the per-call events count then
-    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     t_begin.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    # the same number of calls again, each between its own pair of events on the
+    # launch stream (kernel time per call: average, median, minimum).  Cold-cache
+    # variant: a 1 GiB fill between calls evicts the inputs from L2 and the 256 MB
+    # Infinity Cache; only these per-call events count then.
+    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     for i in range(steps):
         if flush:
             junk.fill_(i & 255)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
-    t_end.record(stream)
     del junk
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     kern_ms = sum(per) / len(per)
     flops = fi.workload_flops(B, H, N, D, causal)

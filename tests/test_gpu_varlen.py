@@ -126,10 +126,15 @@ def test_varlen_workload_sampled(causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_equal_lengths_match_dense(dtype, causal):
     """Equal square sequences, packed head-major, give the same bits as fa_fwd on
-    the [B, H, N, D] layout of the same data (same arithmetic, same order)."""
+    the [B, H, N, D] layout of the same data (same arithmetic, same order).  The
+    grid is large enough that fa_fwd takes whole key tiles per wave (no key
+    groups, whose partials are combined in another order)."""
     import attention_fa_fwd_02_amd as fa
     torch = _torch()
-    B, H, N, D = 3, 2, 700, 64
+    B, H, N, D = 4, 64, 1000, 64
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    name = fa.fa_fwd_kernel_name(B, H, N, D, int(causal), 1 if dtype == "bf16" else 0, n_cus)
+    assert name.endswith(", 1>") or dtype == "f32", name
     q, k, v = fi.make_qkv(B, H, N, D, dtype, seed=77)
     pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(H, B * N, D))
     cu = fi.cu_seqlens([N] * B)
