@@ -30,9 +30,11 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, B4 H16 N4096 D128"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}  # MI355X dense MFMA, published
-# the forward kernel's sources: the kernel file and the device helpers it includes
-KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
-COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_pp_bf16_d128_B4H16N4096_counters.txt")
+# the forward kernel's sources: the kernel file and the device headers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_02_amd", "csrc", f)
+               for f in ("fa_fwd.hip", "fa_fwd_common.h", "fa_device.h")]
+# the headline's rocprofv3 summary (kernel trace, SQ counters, HBM bytes)
+COUNTERS = os.path.join(ROOT, "profiles", "fa_fwd_pp_kernel_bf16_d128_B4H16N4096.txt")
 
 WORKLOADS = {
     # name: (B, H, N, D, dtype, causal, sigma)
