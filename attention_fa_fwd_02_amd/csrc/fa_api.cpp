@@ -137,7 +137,7 @@ const char *fa_status_string(int status) {
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
         return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32, 64/96/128 "
-               "for the backward pass, 64/128 for FP8), fp32 backward, problem too large for "
+               "for the backward pass), fp32 backward, problem too large for "
                "one launch, too many "
                "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
                "device is not gfx950)";
@@ -371,7 +371,7 @@ fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (D != 64 && D != 128)
+    if (D != 64 && D != 96 && D != 128 && D != 192 && D != 256)
         return FA_ERR_UNSUPPORTED;
     // V^T rows are addressed with 32-bit offsets: D * Npad < 2^32
     if (N >= (int64_t(1) << 24) || B >= (int64_t(1) << 31) || H >= (int64_t(1) << 31))

@@ -39,7 +39,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kF8Waves = 8;
 constexpr int kF8Threads = 64 * kF8Waves;
 constexpr int kF8Rows = 32 * kF8Waves; // query rows per workgroup
-constexpr int kF8BC = 128;              // keys per tile
 constexpr int kScaleOne = 127;          // E8M0 block scale 2^0
 constexpr int kF8Ahead = 2;             // MFMAs whose LDS operands are read ahead
 
@@ -104,11 +103,16 @@ __global__ __launch_bounds__(256) void fa_fp8_vt_kernel(const uint8_t *__restric
 // ----------------------------------------------------------------------------
 template <int D>
 struct F8Cfg {
+    // keys per tile: 128, or 64 at D = 256 (the O accumulators take 128
+    // registers there, and two waves per SIMD need the score tile to shrink)
+    static constexpr int BC = D > 192 ? 64 : 128;
     static constexpr int KP = D + 16;        // K row pitch (bytes)
-    static constexpr int VTP = kF8BC + 16;   // V^T row pitch (bytes)
-    static constexpr int NK = kF8BC * KP / 1024;
-    static constexpr int NV = D * VTP / 1024;
-    static_assert(NK * 1024 == kF8BC * KP && NV * 1024 == D * VTP, "tiles are whole 1 KB blocks");
+    static constexpr int VTP = BC + 16;      // V^T row pitch (bytes)
+    static constexpr int NK = BC * KP / 1024;
+    // 1 KB blocks of a V^T tile; at D = 96 the last block is half spare (its
+    // slots lie past the last feature row and read zeros)
+    static constexpr int NV = (D * VTP + 1023) / 1024;
+    static_assert(NK * 1024 == BC * KP, "K tiles are whole 1 KB blocks");
     static constexpr int LPW = (NK + NV + kF8Waves - 1) / kF8Waves; // loads per wave and tile
     static constexpr int OP = 2 * D + 16;    // bf16 O staging pitch
 };
@@ -116,7 +120,11 @@ struct F8Cfg {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     using Cfg = F8Cfg<D>;
-    constexpr int BC = kF8BC, KB = BC / 32, DS = D / 64, OB = D / 32;
+    // DS 64-wide k-steps of the score MFMA; at D = 96 the second step's upper
+    // half (features 96 .. 127, lane half g = 1) has a zero Q operand
+    constexpr int BC = Cfg::BC, KB = BC / 32, DS = (D + 63) / 64, OB = D / 32;
+    constexpr bool HALF_STEP = D % 64 != 0;
+    static_assert(D % 32 == 0, "features in 32-wide MFMA blocks");
     constexpr int KP = Cfg::KP, VTP = Cfg::VTP, OP = Cfg::OP;
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
     constexpr float kLimit = 256.0f; // P~ <= 2^8: within E4M3's range (448)
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     i32x8 qf[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-        if (qi < N) {
+        if (qi < N && 64 * s + 32 * g < D) {
             const u32x4 lo = *(const u32x4 *)(Q + (int64_t)qi * D + 64 * s + 32 * g);
             const u32x4 hi = *(const u32x4 *)(Q + (int64_t)qi * D + 64 * s + 32 * g + 16);
             qf[s] = i32x8{(int)(lo[0] ^ a.qneg), (int)(lo[1] ^ a.qneg), (int)(lo[2] ^ a.qneg), (int)(lo[3] ^ a.qneg),
@@ -236,7 +244,10 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         for (int st = 0; st < DS; ++st)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const lds_char *p = kst + k_lane + 32 * kb * KP + 64 * st;
+                // (the zero half of a half step reads its row's first half instead:
+                // finite bytes inside the tile, multiplied by the zero Q operand)
+                const int kofs = (HALF_STEP && st == DS - 1) ? 64 * st - 32 * g : 64 * st;
+                const lds_char *p = kst + k_lane + 32 * kb * KP + kofs;
                 const u32x4 lo = *(const __attribute__((address_space(3))) u32x4 *)p;
                 const u32x4 hi = *(const __attribute__((address_space(3))) u32x4 *)(p + 16);
                 const i32x8 kv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -394,34 +405,45 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     // epilogue: O = acc * v_descale / l in bf16, staged through LDS; lse
     const float l_tot = pair_sum(l_run);
     const float inv = a.v_descale / l_tot;
-    // every tile read is done; waves 2i and 2i + 1 stage their rows in stage array i
-    static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
-    const int sa = wave >> 1;
+    // every tile read is done; waves 2i and 2i + 1 stage their rows in stage
+    // array i, or (when two waves' rows do not fit an array) waves i and i + 4
+    // use array i in two rounds: waves 0..3 write, read back and store, then
+    // waves 4..7 (every wave passes the same barriers)
+    constexpr bool TWO_ROUNDS = 2 * 32 * OP > KBYTES;
+    constexpr int ROUNDS = TWO_ROUNDS ? 2 : 1;
+    static_assert(32 * OP <= KBYTES, "a wave's O rows fit in a stage array");
+    const int sa = TWO_ROUNDS ? (wave & 3) : (wave >> 1);
     lds_char *const own = sa == 0 ? ks0 : sa == 1 ? ks1 : sa == 2 ? vs0 : vs1;
-    lds_char *ow = own + (wave & 1) * 32 * OP;
-    if (q0w < N) {
+    lds_char *ow = own + (TWO_ROUNDS ? 0 : (wave & 1) * 32 * OP);
 #pragma unroll
-        for (int b = 0; b < OB; ++b)
+    for (int round = 0; round < ROUNDS; ++round) {
+        const bool mine = !TWO_ROUNDS || (wave >> 2) == round;
+        if (mine && q0w < N) {
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const u32x2 w = {Bf16::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
-                                 Bf16::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
-                *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
-            }
-        if (g == 0 && qi < N)
-            LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    }
-    __syncthreads();
-    if (q0w < N) {
+            for (int b = 0; b < OB; ++b)
 #pragma unroll
-        for (int j = 0; j < 32 * (D / 8) / 64; ++j) {
-            const int ch = 64 * j + lane;
-            const int row = ch / (D / 8), col = ch % (D / 8);
-            const int q = q0w + row;
-            const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
-            if (q < N)
-                *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const u32x2 w = {Bf16::pack(o[b][4 * a4] * inv, o[b][4 * a4 + 1] * inv),
+                                     Bf16::pack(o[b][4 * a4 + 2] * inv, o[b][4 * a4 + 3] * inv)};
+                    *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
+                }
+            if (g == 0 && qi < N)
+                LSE[qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
         }
+        __syncthreads();
+        if (mine && q0w < N) {
+#pragma unroll
+            for (int j = 0; j < 32 * (D / 8) / 64; ++j) {
+                const int ch = 64 * j + lane;
+                const int row = ch / (D / 8), col = ch % (D / 8);
+                const int q = q0w + row;
+                const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(ow + row * OP + col * 16);
+                if (q < N)
+                    *(u32x4 *)(O + (int64_t)q * D + col * 8) = val;
+            }
+        }
+        if (round + 1 < ROUNDS)
+            __syncthreads(); // the next round's rows go where this round's were read
     }
 }
 
@@ -444,7 +466,18 @@ hipError_t launch_fp8_t(bool causal, int64_t BH, const Fp8Args &args, hipStream_
 } // namespace
 
 hipError_t launch_fp8(int D, bool causal, int64_t BH, const Fp8Args &args, hipStream_t stream) {
-    return D == 64 ? launch_fp8_t<64>(causal, BH, args, stream) : launch_fp8_t<128>(causal, BH, args, stream);
+    switch (D) {
+    case 64:
+        return launch_fp8_t<64>(causal, BH, args, stream);
+    case 96:
+        return launch_fp8_t<96>(causal, BH, args, stream);
+    case 192:
+        return launch_fp8_t<192>(causal, BH, args, stream);
+    case 256:
+        return launch_fp8_t<256>(causal, BH, args, stream);
+    default:
+        return launch_fp8_t<128>(causal, BH, args, stream);
+    }
 }
 
 } // namespace fa

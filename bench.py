@@ -375,15 +375,18 @@ def bench_bwd(name, steps, warmup):
 
 
 def bench_fp8(name, steps, warmup):
-    """fa_fwd_fp8 on the headline shape (B4 H16 N4096 D128, E4M3 inputs, bf16 O;
-    stderr line only).  FLOPs as for the 16-bit path; peak: dense FP8 MFMA."""
+    """fa_fwd_fp8 on the headline shape (B4 H16 N4096 D128, E4M3 inputs, bf16 O),
+    or B4 H8 N4096 at head dim 96 / 192 / 256 (stderr line only).  FLOPs as for
+    the 16-bit path; peak: dense FP8 MFMA."""
     import numpy as np
     import torch
 
     import attention_fa_fwd_02_amd as fa
     import fa_inputs as fi
     causal = name.endswith("causal")
-    B, H, N, D = 4, 16, 4096, 128
+    # fp8 / fp8_causal: the headline shape; fp8_d<D>[_causal]: B4 H8 N4096 at head dim D
+    D = int(name.split("_d")[1].split("_")[0]) if "_d" in name else 128
+    B, H, N = (4, 16, 4096) if D == 128 else (4, 8, 4096)
     q, k, v = fi.make_qkv(B, H, N, D, "e4m3", 1004)
     dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (q, k, v))
     o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device="cuda")
@@ -471,7 +474,7 @@ def main():
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("fp8", "fp8_causal"):
+        for name in ("fp8", "fp8_causal", "fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     if args.flush:
         for name in ("headline", "headline_causal"):
