@@ -469,7 +469,7 @@ def main():
         # work would otherwise leave the GPU idle (and down-clocked) right before
         for name in list(WORKLOADS) + list(SPLIT_WORKLOADS):
             if name != args.workload:
-                bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5))
+                bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), warm_seconds=0.5)
         for name in ("varlen", "varlen_causal"):
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal"):

@@ -16,9 +16,9 @@ Two derived adjustments:
     other scales;
   * the bf16/fp16 paths round the weights P~ to the input type before P~ V
     (relative error u_P = 2^-9 for bf16, 2^-12 for fp16), so a row dominated by
-    one key carries an error up to u_P * |v|.  The workloads' diffuse softmax
-    (scale 1/sqrt(D), N(0,1) inputs) averages it away and is held to 1e-2;
-    the sharp-softmax stress cases (other scales) get 1e-2 + u_P * max|V|.
+    one key carries an error up to u_P * |v|.  Every case, the sharp-softmax
+    stress scales included, is still held to 1e-2 (the stress cases print
+    their margin to it).
 """
 import math
 import sys
@@ -149,17 +149,11 @@ def check_case(B, H, N, D, dtype, causal, seed, sigma=(1.0, 1.0, 1.0), scale=Non
     if dtype == "f32":
         f = max(1.0, abs(scale) * math.sqrt(D))
         to, tl = to * f, tl * f
-    elif abs(abs(scale) * math.sqrt(D) - 1.0) > 1e-6:
-        u_p = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12}[dtype]
-        to = to + u_p * float(np.abs(oracle.widen(v, dtype)).max())
     eo, el, mo, ex, nbig = compare(q, k, v, dtype, scale, causal, o, lse, slices, rows_of, to)
     print("  max|dO|=%.3g max|dlse|=%.3g max|O|=%.3g  tol O %.3g lse %.3g  (%d elements with |O|>=4)"
           % (eo, el, mo, to, tl, nbig), flush=True)
-    if dtype != "f32" and to > TOL[dtype][0]:
-        # the same comparison against the unwidened bound (the excess differs by a constant)
-        plain = ex + (to - TOL[dtype][0])
-        print("  stress scale %g: margin to the unwidened %.0e bound %.3g (%s)"
-              % (scale, TOL[dtype][0], -plain, "holds" if plain <= 0.0 else "exceeded"), flush=True)
+    if dtype != "f32" and abs(abs(scale) * math.sqrt(D) - 1.0) > 1e-6:
+        print("  stress scale %g: margin to the %.0e bound %.3g" % (scale, to, -ex), flush=True)
     assert ex <= 0.0, (eo, to, ex)
     assert el <= tl, (el, tl)
     return o, lse
