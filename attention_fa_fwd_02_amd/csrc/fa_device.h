@@ -80,17 +80,21 @@ struct Work {
 // contiguous logical range [x * n/8, (x+1) * n/8), so the query blocks of a
 // slice share one L2.  Causal query blocks differ in length (block qb has
 // qb + 1 blocks' worth of keys): when each XCD's range holds whole slices,
-// they are handed out longest first across the XCD's slices, so the short
-// ones fill in at the end instead of a long one starting last.
+// they are handed out longest first, so the short ones fill in at the end
+// instead of a long one starting last.  The XCD's slices are taken four at a
+// time (longest first within each group of four), so that fewer slices' K
+// and V are read through the XCD's L2 at once.
 __device__ __forceinline__ Work map_workgroup(int wg, int nwg, int n_qblk, bool causal) {
     Work w;
     if ((nwg & 7) == 0) {
         const int per = nwg >> 3;
         const int x = wg & 7, j = wg >> 3;
         if (causal && per % n_qblk == 0) {
-            const int hx = per / n_qblk; // slices per XCD
-            w.bh = x * hx + j % hx;
-            w.qb = n_qblk - 1 - j / hx;
+            const int hx = per / n_qblk;             // slices per XCD
+            const int gs = (hx & 3) == 0 ? 4 : hx;   // slices per group
+            const int gsz = gs * n_qblk, grp = j / gsz, in = j - grp * gsz;
+            w.bh = x * hx + grp * gs + in % gs;
+            w.qb = n_qblk - 1 - in / gs;
             return w;
         }
         const int L = x * per + j;

@@ -69,6 +69,7 @@
 #include <atomic>
 #include <cstdio>
 #include <mutex>
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -162,25 +163,40 @@ struct MfmaCfg {
     static constexpr bool PINGPONG = WAVES == 8 && BC == 128;
 };
 
-// Per-lane byte offsets of the tile loader, two 16-bit offsets per register.
-// Load j of wave w fills 1 KB block b = w + WAVES j of a stage: blocks below
-// NK hold the K tile (row pitch KP), the next NV the V tile (pitch VP), the
-// rest are spare.  Lane l of a load writes stage byte 1024 b + 16 l; the
-// offset is that byte's position in the tile's rows of D 16-bit features
-// (a lane whose slot falls in a row's padding, or a spare block, re-reads the
-// row's first chunk; those bytes are never read back).
-template <int D>
-__device__ __forceinline__ void tile_offsets(uint32_t (&voff2)[(MfmaCfg<D>::LPW + 1) / 2], int wave, int lane) {
+// Position of the i-th of NL tile loads among NM MFMAs of one phase: after
+// every STRIDE-th MFMA and none among the last four, or all after the first
+// MFMA when the phase has no more than four.  Every position is in [0, NM),
+// so every load is issued.
+template <int NL, int NM>
+__device__ constexpr int load_at(int i) {
+    constexpr int SPAN = NM > 4 ? NM - 4 : 1;
+    constexpr int STRIDE = SPAN / (NL > 0 ? NL : 1) > 0 ? SPAN / (NL > 0 ? NL : 1) : 1;
+    return i * STRIDE < SPAN ? i * STRIDE : SPAN - 1;
+}
+static_assert(load_at<9, 4>(8) == 0 && load_at<9, 8>(8) == 3 && load_at<9, 32>(8) == 24 && load_at<9, 6>(3) == 1,
+              "load positions stay among the MFMAs");
+
+// Per-lane byte offsets of a tile loader in which IW waves issue LPI loads
+// each, two 16-bit offsets per register.  Load j of issuing wave w fills 1 KB
+// block b = w + IW j of a stage: blocks below NK hold the K tile (row pitch
+// KP), the next NV the V tile (pitch VP), the rest are spare.  Lane l of a
+// load writes stage byte 1024 b + 16 l; the offset is that byte's position in
+// the tile's rows of D 16-bit features (a lane whose slot falls in a row's
+// padding, or a spare block, re-reads the row's first chunk; those bytes are
+// never read back).
+template <int D, int IW, int LPI>
+__device__ __forceinline__ void tile_offsets_iw(uint32_t (&voff2)[(LPI + 1) / 2], int wave, int lane) {
     using Cfg = MfmaCfg<D>;
-    constexpr int W = Cfg::WAVES, NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW, KP = Cfg::KP, VP = Cfg::VP;
+    constexpr int NK = Cfg::NK, NV = Cfg::NV, KP = Cfg::KP, VP = Cfg::VP;
     constexpr int KCH = D / 8; // 16-byte chunks per K/V row
     static_assert(Cfg::BC * D * 2 <= 32768, "tile offsets fit in 16 bits");
+    static_assert(IW * LPI >= NK + NV, "the loads cover the tile");
 #pragma unroll
-    for (int j = 0; j < (LPW + 1) / 2; ++j)
+    for (int j = 0; j < (LPI + 1) / 2; ++j)
         voff2[j] = 0u;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int blk = wave + W * j;
+    for (int j = 0; j < LPI; ++j) {
+        const int blk = wave + IW * j;
         const bool is_k = blk < NK, is_v = !is_k && blk < NK + NV;
         const int pitch = is_k ? KP : VP;
         const int pos = 1024 * (is_k ? blk : blk - NK) + 16 * lane;
@@ -188,6 +204,11 @@ __device__ __forceinline__ void tile_offsets(uint32_t (&voff2)[(MfmaCfg<D>::LPW 
         const uint32_t off = (is_k || is_v) ? (uint32_t)((pos / pitch) * D + (chunk < KCH ? 8 * chunk : 0)) * 2u : 0u;
         voff2[j / 2] |= off << (16 * (j % 2));
     }
+}
+// every wave of the workgroup issues LPW loads
+template <int D>
+__device__ __forceinline__ void tile_offsets(uint32_t (&voff2)[(MfmaCfg<D>::LPW + 1) / 2], int wave, int lane) {
+    tile_offsets_iw<D, MfmaCfg<D>::WAVES, MfmaCfg<D>::LPW>(voff2, wave, lane);
 }
 
 // The fp32 partial result of a key split: O / l (0 for a row that saw no key
@@ -607,31 +628,53 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int k_begin = SPLIT ? blk.k_begin : 0, kv_end = blk.kv_end, n_tiles = blk.n_tiles;
 
     // --- loader: batch b = the K rows of tile b and the V rows of tile b - 1 --
-    // Load j of wave w fills 1 KB block w + 8j: blocks below NK go to the K
-    // stage, the rest to the V stage (the V tile, then spare blocks that
-    // re-read the tile's first row).  Descriptors stop at kv_end: rows past it
-    // read as zeros.
-    uint32_t voff2[(LPW + 1) / 2];
-    tile_offsets<D>(voff2, wave, lane);
-    auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
+    // Load j of issuing wave w fills 1 KB block w + IW j: blocks below NK go
+    // to the K stage, the rest to the V stage (the V tile, then spare blocks
+    // that re-read the tile's first row).  Descriptors stop at kv_end: rows
+    // past it read as zeros.
+    // Without the causal mask the IW = 4 waves of group 0 issue every load of
+    // a batch (18 each), spread among the MFMAs of their M phase.  Issued back
+    // to back by all eight waves at the start of a phase, the loads stall
+    // every issuing wave until the address unit has taken them (about 16
+    // cycles per 1 KB load, over 1k cycles per batch).  Causal instances keep
+    // the burst (all eight waves, 9 loads each, at the start of phase 2c): the
+    // spread loader's offsets take registers they do not have.
+    constexpr bool SPREAD = !CAUSAL;
+    constexpr int IW = SPREAD ? 4 : W, LPI = (NK + NV + IW - 1) / IW;
+    static_assert(IW * LPI == W * LPW, "same stage layout");
+    const int iwave = SPREAD ? (wave & 3) : wave;
+    uint32_t voff2[(LPI + 1) / 2];
+    tile_offsets_iw<D, IW, LPI>(voff2, iwave, lane);
+    struct Batch {
+        const uint16_t *kb, *vb;
+        uint32_t kbytes, vbytes;
+        lds_char *kd, *vd;
+    };
+    auto batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
         const int kk = k_begin + b * BC, kv = k_begin + max(b - 1, 0) * BC;
-        const uint32_t kbytes =
-            __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D * 2 : 0));
-        const uint32_t vbytes = __builtin_amdgcn_readfirstlane(
+        Batch x;
+        x.kbytes = __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D * 2 : 0));
+        x.vbytes = __builtin_amdgcn_readfirstlane(
             (uint32_t)(b >= 1 && b - 1 < n_tiles ? min(kv_end - kv, BC) * D * 2 : 0));
-        const uint16_t *const kb_ = K + (int64_t)kk * D;
-        const uint16_t *const vb_ = V + (int64_t)kv * D;
+        x.kb = K + (int64_t)kk * D;
+        x.vb = V + (int64_t)kv * D;
+        x.kd = kd;
+        x.vd = vd;
+        return x;
+    };
+    // load j of this wave (K or V block chosen by selects, not branches)
+    auto load_one = [&](const Batch &x, int j) __attribute__((always_inline)) {
+        const int blk = iwave + IW * j; // wave-uniform
+        const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+        const bool isk = blk < NK;
+        load_lds_16(isk ? x.kb : x.vb, isk ? x.kbytes : x.vbytes, off,
+                    isk ? x.kd + 1024 * blk : x.vd + 1024 * (blk - NK));
+    };
+    auto load_range = [&](const Batch &x, int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int blk = wave + W * j; // wave-uniform
-            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
-            // K or V block chosen by selects, not branches
-            const bool isk = blk < NK;
-            const uint16_t *base = isk ? kb_ : vb_;
-            const uint32_t bytes = isk ? kbytes : vbytes;
-            lds_char *dst = isk ? kd + 1024 * blk : vd + 1024 * (blk - NK);
-            load_lds_16(base, bytes, off, dst);
-        }
+        for (int j = 0; j < LPI; ++j)
+            if (j >= j0 && j < j1)
+                load_one(x, j);
     };
     const int k_lane = (8 * (r >> 3) + 2 * (r & 3) + ((r >> 2) & 1)) * KP + 16 * g;
     const int v_lane = (g + 2 * ((lane >> 2) & 3)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
@@ -660,7 +703,8 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
         }
     };
     // S^T = K Q^T : s[kb][i] = score(query qi, key k0 + 32kb + 2i + g)
-    auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
+    auto scores = [&](const lds_char *kst, const Batch &x, int j0, auto nl) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value, NM = KB * DC;
         const lds_char *ks = kst + k_lane + kws * KP;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -671,20 +715,30 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
             for (int kb = 0; kb < KB; ++kb) {
                 const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(ks + 32 * kb * KP + 32 * cc);
                 s[kb] = E::mfma(kv, qf[cc], s[kb]);
+#pragma unroll
+                for (int i = 0; i < NL; ++i)
+                    if (load_at<NL, NM>(i) == cc * KB + kb)
+                        load_one(x, j0 + i);
             }
-        // four K reads ahead of the MFMAs, then one read per MFMA
+        // four K reads ahead of the MFMAs, then one read per MFMA (and the
+        // loads where placed)
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int n = 0; n < KB * DC - 4; ++n) {
+        for (int n = 0; n < NM - 4; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (load_at<NL, NM>(i) == n)
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     // O^T += V^T P^T : o[b][i] accumulates feature 32b + 8(i/4) + 4g + i%4 of
     // query qi.  Consecutive MFMAs go to different accumulators; each o[b]
     // still adds its (kb, mm) terms in order.
-    auto accumulate = [&](const lds_char *vst) __attribute__((always_inline)) {
+    auto accumulate = [&](const lds_char *vst, const Batch &x, int j0, auto nl) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value, NM = OB * KB * 2;
         const lds_char *vs = vst + v_lane + kws * VP;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -702,13 +756,22 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
                     const u32x4 vv = {l2[0], l2[1], h2[0], h2[1]};
                     const u32x4 pb = {pk[kb][4 * mm], pk[kb][4 * mm + 1], pk[kb][4 * mm + 2], pk[kb][4 * mm + 3]};
                     o[b] = E::mfma(vv, pb, o[b]);
+#pragma unroll
+                    for (int i = 0; i < NL; ++i)
+                        if (load_at<NL, NM>(i) == (kb * 2 + mm) * OB + b)
+                            load_one(x, j0 + i);
                 }
-        // eight transposing reads (four MFMAs) ahead, then two per MFMA
+        // eight transposing reads (four MFMAs) ahead, then two per MFMA (and
+        // the loads where placed)
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int n = 0; n < OB * KB * 2 - 4; ++n) {
+        for (int n = 0; n < NM - 4; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (load_at<NL, NM>(i) == n)
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
@@ -719,18 +782,39 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
             mask_keys<KB, CAUSAL>(s, k0, N, qi, 0, g);
         online_softmax<E, KB, OB>(s, pk, o, m_run, l_run, c);
     };
+    using none_t = std::integral_constant<int, 0>;
     auto M = [&](int t, const lds_char *vprev, const lds_char *kcur) __attribute__((always_inline)) {
+        const Batch none{};
         if (t >= 1 && t - 1 < n_tiles && active(t - 1))
-            accumulate(vprev);
+            accumulate(vprev, none, 0, none_t{});
         if (t < n_tiles && active(t))
-            scores(kcur);
+            scores(kcur, none, 0, none_t{});
+    };
+    // group 0 with the spread loader: M(t) with the loads of batch t + 1
+    // among its MFMAs (half among the PV MFMAs, half among the score MFMAs;
+    // a skipped half issues its loads directly).  Past the last tile the
+    // batch has zero-length descriptors: its loads write zeros to stages no
+    // later phase reads.
+    constexpr int LA = LPI / 2, LB = LPI - LA;
+    auto ML = [&](int t, const lds_char *vprev, const lds_char *kcur, lds_char *kn, lds_char *vn)
+                  __attribute__((always_inline)) {
+        const Batch x = batch(t + 1, kn, vn);
+        if (t >= 1 && t - 1 < n_tiles && active(t - 1))
+            accumulate(vprev, x, 0, std::integral_constant<int, LA>{});
+        else
+            load_range(x, 0, LA);
+        if (t < n_tiles && active(t))
+            scores(kcur, x, LA, std::integral_constant<int, LB>{});
+        else
+            load_range(x, LA, LPI);
     };
     auto X = [&](int t) __attribute__((always_inline)) {
         if (t >= 0 && t < n_tiles && active(t))
             softmax(t);
     };
 
-    issue_batch(0, ks0, vs1);
+    if (!SPREAD || grp == 0)
+        load_range(batch(0, ks0, vs1), 0, LPI);
     wait_vmcnt<0>();
     tile_barrier();
     // Phase 2c: batch c + 1 goes out; group 0 runs M(c), group 1 X(c - 1).
@@ -740,9 +824,13 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     if (grp == 0) {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            if (cc + 1 <= n_tiles)
-                issue_batch(cc + 1, kn, vn);
-            M(cc, vprev, kcur);
+            if constexpr (SPREAD) {
+                ML(cc, vprev, kcur, kn, vn);
+            } else {
+                if (cc + 1 <= n_tiles)
+                    load_range(batch(cc + 1, kn, vn), 0, LPI);
+                M(cc, vprev, kcur);
+            }
             tile_barrier();
             X(cc);
             wait_vmcnt<0>();
@@ -758,8 +846,8 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     } else {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            if (cc + 1 <= n_tiles)
-                issue_batch(cc + 1, kn, vn);
+            if (!SPREAD && cc + 1 <= n_tiles)
+                load_range(batch(cc + 1, kn, vn), 0, LPI);
             X(cc - 1);
             tile_barrier();
             M(cc, vprev, kcur);
