@@ -636,10 +636,12 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     // a batch (18 each), spread among the MFMAs of their M phase.  Issued back
     // to back by all eight waves at the start of a phase, the loads stall
     // every issuing wave until the address unit has taken them (about 16
-    // cycles per 1 KB load, over 1k cycles per batch).  Causal instances keep
-    // the burst (all eight waves, 9 loads each, at the start of phase 2c): the
-    // spread loader's offsets take registers they do not have.
-    constexpr bool SPREAD = !CAUSAL;
+    // cycles per 1 KB load, over 1k cycles per batch).  Causal instances of
+    // whole-tile waves at D = 96 and 128 keep the burst (all eight waves, 9
+    // loads each, at the start of phase 2c): at D = 128 the spread loader's
+    // offsets leave them short of registers (they spill), at D = 96 it
+    // measured no faster.
+    constexpr bool SPREAD = !CAUSAL || KG > 1 || D == 64;
     constexpr int IW = SPREAD ? 4 : W, LPI = (NK + NV + IW - 1) / IW;
     static_assert(IW * LPI == W * LPW, "same stage layout");
     const int iwave = SPREAD ? (wave & 3) : wave;

@@ -1,9 +1,10 @@
-// Device building blocks shared by the forward kernels (fa_fwd.hip and
-// fa_fwd_w64.hip): the Q operand load, the masks of a transposed score tile,
-// the online softmax of one tile against the running reference, and the O
-// epilogue.  The layouts are those of the v_mfma_f32_32x32x16 S^T = K Q^T
-// tiles: lane (r, g) holds query row r of a 32-row block, and accumulator
-// entry i of lane half g is key 2i + g of a 32-key block.
+// Device building blocks of the 16-bit forward kernels in fa_fwd.hip (the
+// one-barrier and the ping-pong kernel): the Q operand load, the masks of a
+// transposed score tile, the online softmax of one tile against the running
+// reference, and the O epilogue.  The layouts are those of the
+// v_mfma_f32_32x32x16 S^T = K Q^T tiles: lane (r, g) holds query row r of a
+// 32-row block, and accumulator entry i of lane half g is key 2i + g of a
+// 32-key block.
 #pragma once
 #include "fa_device.h"
 
