@@ -632,16 +632,19 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     // to the K stage, the rest to the V stage (the V tile, then spare blocks
     // that re-read the tile's first row).  Descriptors stop at kv_end: rows
     // past it read as zeros.
-    // Without the causal mask the IW = 4 waves of group 0 issue every load of
-    // a batch (18 each), spread among the MFMAs of their M phase.  Issued back
-    // to back by all eight waves at the start of a phase, the loads stall
-    // every issuing wave until the address unit has taken them (about 16
-    // cycles per 1 KB load, over 1k cycles per batch).  Causal instances of
-    // whole-tile waves at D = 96 and 128 keep the burst (all eight waves, 9
-    // loads each, at the start of phase 2c): at D = 128 the spread loader's
-    // offsets leave them short of registers (they spill), at D = 96 it
-    // measured no faster.
-    constexpr bool SPREAD = !CAUSAL || KG > 1 || D == 64;
+    // Issued back to back by all eight waves at the start of a phase, the
+    // loads stall every issuing wave until the address unit has taken them
+    // (about 16 cycles per 1 KB load, over 1k cycles per batch); a stall in
+    // an M phase holds up the matrix core.  Two loaders keep the loads off
+    // the M waves' critical path:
+    //  - spread: the IW = 4 waves of group 0 issue every load of a batch (18
+    //    each) among the MFMAs of their M phase, one after every third MFMA;
+    //  - split burst (whole-tile waves at D = 128, and causal ones at D = 96):
+    //    every wave issues its 9 loads at the start of its own X phase, group
+    //    1 in phase 2c and group 0 in phase 2c + 1, where the softmax work
+    //    leaves slack.  (At D = 128 the spread loader's 18 offsets per wave
+    //    would also make the causal instances spill.)
+    constexpr bool SPREAD = !(KG == 1 && (D == 128 || (D == 96 && CAUSAL)));
     constexpr int IW = SPREAD ? 4 : W, LPI = (NK + NV + IW - 1) / IW;
     static_assert(IW * LPI == W * LPW, "same stage layout");
     const int iwave = SPREAD ? (wave & 3) : wave;
@@ -819,21 +822,24 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
         load_range(batch(0, ks0, vs1), 0, LPI);
     wait_vmcnt<0>();
     tile_barrier();
-    // Phase 2c: batch c + 1 goes out; group 0 runs M(c), group 1 X(c - 1).
-    // Phase 2c + 1: group 0 runs X(c), group 1 M(c); batch c + 1 has landed.
+    // Phase 2c: batch c + 1 goes out (spread: among group 0's MFMAs; split
+    // burst: group 1's half); group 0 runs M(c), group 1 X(c - 1).
+    // Phase 2c + 1: (split burst: group 0's half of batch c + 1 goes out)
+    // group 0 runs X(c), group 1 M(c); batch c + 1 has landed at its end.
     // Each group runs a straight-line loop of its own; both pass the same
     // number of barriers.  Tile c is in stage c % 2.
     if (grp == 0) {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            if constexpr (SPREAD) {
+            if constexpr (SPREAD)
                 ML(cc, vprev, kcur, kn, vn);
-            } else {
-                if (cc + 1 <= n_tiles)
-                    load_range(batch(cc + 1, kn, vn), 0, LPI);
+            else
                 M(cc, vprev, kcur);
-            }
             tile_barrier();
+            // (split burst: batch c + 1 goes to stages no wave reads in this
+            // phase, and has landed by the barrier that ends it)
+            if (!SPREAD && cc + 1 <= n_tiles)
+                load_range(batch(cc + 1, kn, vn), 0, LPI);
             X(cc);
             wait_vmcnt<0>();
             tile_barrier();
