@@ -127,14 +127,18 @@ struct TilePair {
     // rows row0 .. row0 + R - 1 of X and Y; rows at or past n_rows read as zeros
     __device__ __forceinline__ void issue(const uint16_t *X, const uint16_t *Y, int row0, int n_rows,
                                           lds_char *st, int wave) const {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j)
+            issue_one(X, Y, row0, n_rows, st, wave, j);
+    }
+    // load j of this wave alone
+    __device__ __forceinline__ void issue_one(const uint16_t *X, const uint16_t *Y, int row0, int n_rows,
+                                              lds_char *st, int wave, int j) const {
         const uint32_t bytes =
             __builtin_amdgcn_readfirstlane((uint32_t)(min(max(n_rows - row0, 0), R) * D * 2));
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int blk = wave + W * j;
-            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
-            load_lds_16((blk >= NX && blk < 2 * NX ? Y : X) + (int64_t)row0 * D, bytes, off, st + 1024 * blk);
-        }
+        const int blk = wave + W * j;
+        const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+        load_lds_16((blk >= NX && blk < 2 * NX ? Y : X) + (int64_t)row0 * D, bytes, off, st + 1024 * blk);
     }
 };
 
@@ -424,11 +428,21 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
     // 32 (l/32) + 2 (l%16) + (l/16)%2 of the tile, so a lane half g finds the
     // queries of its accumulator entries (2i + g) as 16 consecutive floats
     const uint32_t stat_off = 4u * (uint32_t)(32 * (lane >> 5) + 2 * (lane & 15) + ((lane >> 4) & 1));
-    auto issue = [&](int t, lds_char *st) {
+    // load j (0 .. NLD - 1) of tile t: the wave's Q / dO blocks, then its lse / Delta load
+    constexpr int NLD = Tiles::LPW + 1;
+    auto issue_one = [&](int t, lds_char *st, int j) __attribute__((always_inline)) {
         const int i0 = t * TQ;
-        tiles.issue(Q, dO, i0, N, st, wave);
-        const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(min(max(N - i0, 0), TQ) * 4));
-        load_lds_4((wave == 1 ? DL : LSE) + i0, sb, stat_off, st + STAT + 256 * wave);
+        if (j < Tiles::LPW) {
+            tiles.issue_one(Q, dO, i0, N, st, wave, j);
+        } else {
+            const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(min(max(N - i0, 0), TQ) * 4));
+            load_lds_4((wave == 1 ? DL : LSE) + i0, sb, stat_off, st + STAT + 256 * wave);
+        }
+    };
+    auto issue = [&](int t, lds_char *st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+            issue_one(t, st, j);
     };
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const int q_lane = perm_row(r) * P + 16 * g;
@@ -529,20 +543,43 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
                 }
             };
+            // the next tile's loads go out among the first MFMAs of the tile,
+            // one after each (issued back to back they stall the wave, and with
+            // one wave per SIMD the matrix core with it); at D = 64 the last
+            // ones go among the next section's MFMAs, one after every other
+            constexpr int L0 = (2 * DC - 4) < NLD ? (2 * DC - 4) : NLD;
             sdp(0);
+#pragma unroll
+            for (int j = 0; j < L0; ++j)
+                issue_one(t + 1, next, j);
             // four operand reads ahead of the first half's S / dP MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int n = 0; n < 2 * DC - 4; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (n < L0)
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            issue(t + 1, next);
             __builtin_amdgcn_sched_barrier(0);
             sdp(1);
             soft(0);
-            interleave(std::integral_constant<int, 2 * DC>{}, std::integral_constant<int, 1>{});
+#pragma unroll
+            for (int j = L0; j < NLD; ++j)
+                issue_one(t + 1, next, j);
+            {
+                constexpr int NM = 2 * DC, RP = 1, L1 = NLD - L0;
+                __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+                for (int n = 0; n < NM; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, RP, 0); // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                    if (n % 2 == 0 && n / 2 < L1)
+                        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             grad(0);
             soft(1);
