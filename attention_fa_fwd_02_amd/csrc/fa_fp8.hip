@@ -357,9 +357,10 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
 
     // Ping-pong schedule (as in the 16-bit dense kernel): waves 4..7 run one
     // phase behind waves 0..3, so on every SIMD one wave issues MFMAs while
-    // the other does its softmax.  Phase 2c: batch c + 1 goes out; group 0
-    // runs M(c), group 1 X(c - 1).  Phase 2c + 1: group 0 runs X(c), group 1
-    // M(c); batch c + 1 has landed at its end.
+    // the other does its softmax.  Phase 2c: group 1 issues its half of batch
+    // c + 1 and runs X(c - 1), group 0 runs M(c).  Phase 2c + 1: group 0
+    // issues its half and runs X(c), group 1 M(c); batch c + 1 has landed at
+    // its end (the stages it fills are read by neither phase).
     const int grp = wave >> 2;
     issue_batch(0, ks0, vs1);
     wait_vmcnt<0>();
@@ -367,10 +368,14 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     if (grp == 0) {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            if (cc + 1 <= n_tiles)
-                issue_batch(cc + 1, kn, vn);
             M(cc, vprev, kcur);
             tile_barrier();
+            // (group 0 issues its half of batch c + 1 here, at the start of its
+            // softmax phase: at the start of an M phase the loads would stall
+            // the wave, and the matrix core with it, until the address unit
+            // has taken them)
+            if (cc + 1 <= n_tiles)
+                issue_batch(cc + 1, kn, vn);
             X(cc);
             wait_vmcnt<0>();
             tile_barrier();

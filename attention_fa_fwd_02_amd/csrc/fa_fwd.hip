@@ -410,17 +410,19 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
     constexpr int NK = Cfg::NK, NV = Cfg::NV, LPW = Cfg::LPW;
     uint32_t voff2[(LPW + 1) / 2];
     tile_offsets<D>(voff2, wave, lane);
-    auto issue_tile = [&](int t, lds_char *st) {
+    auto issue_one = [&](int t, lds_char *st, int j) __attribute__((always_inline)) {
         const int k0 = k_begin + t * BC;
         const uint32_t bytes =
             __builtin_amdgcn_readfirstlane((uint32_t)(min(max(kv_end - k0, 0), BC) * D * 2)); // uniform
+        const int blk = wave + W * j; // wave-uniform
+        const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+        load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, off,
+                    st + 1024 * (wave + W * j));
+    };
+    auto issue_tile = [&](int t, lds_char *st) {
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int blk = wave + W * j; // wave-uniform
-            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
-            load_lds_16((blk >= NK && blk < NK + NV ? V : K) + (int64_t)k0 * D, bytes, off,
-                        st + 1024 * (wave + W * j));
-        }
+        for (int j = 0; j < LPW; ++j)
+            issue_one(t, st, j);
     };
 
     // --- per-lane LDS read bases --------------------------------------------
@@ -459,24 +461,39 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 s[kb] = f32x16{};
+            // The next tile's loads: for square slices spread among the score
+            // MFMAs (issued back to back, a wave's loads stall it until the
+            // address unit has taken them, and at D = 256 a SIMD runs one
+            // wave); for packed sequences after the score phase (spread, the
+            // causal instance spills).
+            constexpr bool SPREAD = !VARLEN;
+            constexpr int NM = KB * DC;
 #pragma unroll
             for (int cc = 0; cc < DC; ++cc)
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(ks + 32 * kb * KP + 32 * cc);
                     s[kb] = E::mfma(kv, qf[cc], s[kb]);
+#pragma unroll
+                    for (int j = 0; j < LPW; ++j)
+                        if (SPREAD && load_at<LPW, NM>(j) == cc * KB + kb)
+                            issue_one(t + 1, next, j);
                 }
             // schedule: four K reads ahead of the MFMAs, then one read per MFMA
+            // (and the loads where placed)
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int n = 0; n < KB * DC - 4; ++n) {
+            for (int n = 0; n < NM - 4; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int j = 0; j < LPW; ++j)
+                    if (SPREAD && load_at<LPW, NM>(j) == n)
+                        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            // the next tile's loads go out after the score phase, so their LDS
-            // writes do not land among its K reads
-            issue_tile(t + 1, next);
+            if (!SPREAD)
+                issue_tile(t + 1, next);
             // masking: keys beyond Nk, and keys after the query when causal
             if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff)) {
                 if constexpr (VARLEN)
