@@ -31,6 +31,8 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -164,10 +166,21 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     // b - 1.  Load j of wave w fills 1 KB block w + 8 j: blocks [0, NK) go to
     // the K stage (rows in MFMA row order), the rest to the V^T stage
     // (feature rows of 128 keys, then spare blocks).
-    uint32_t voff[LPW];
+    // Loads, as in the 16-bit ping-pong kernel: spread, the four waves of
+    // group 0 issue every load of a batch among the MFMAs of their M phase;
+    // split burst (D = 256, and causal D = 192, whose spread instances would
+    // spill), every wave issues its share at the start of its own softmax
+    // phase.  Issued back to back by all eight waves at the start of a
+    // phase, the loads stall every issuing wave until the address unit has
+    // taken them.
+    constexpr bool SPREAD = D <= 128 || (D == 192 && !CAUSAL);
+    constexpr int IW = SPREAD ? 4 : kF8Waves, LPI = (NK + NV + IW - 1) / IW;
+    static_assert(IW * LPI <= kF8Waves * LPW, "the loads fit the stage");
+    const int iwave = SPREAD ? (wave & 3) : wave;
+    uint32_t voff[LPI];
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int blk = wave + kF8Waves * j;
+    for (int j = 0; j < LPI; ++j) {
+        const int blk = iwave + IW * j;
         uint32_t off = 0;
         if (blk < NK) {
             const int pos = 1024 * blk + 16 * lane;
@@ -182,21 +195,23 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         voff[j] = off;
     }
     const uint32_t vt_bytes = __builtin_amdgcn_readfirstlane((uint32_t)D * (uint32_t)Npad);
-    auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
+    auto load_one = [&](int b, lds_char *kd, lds_char *vd, int j) __attribute__((always_inline)) {
         const int kk = b * BC, kv = max(b - 1, 0) * BC;
         const uint32_t k_bytes =
             __builtin_amdgcn_readfirstlane((uint32_t)(b < n_tiles ? min(kv_end - kk, BC) * D : 0));
         // V^T rows hold keys up to Npad (zero-padded); past the last tile nothing is read
         const uint32_t v_bytes = (b >= 1 && b - 1 < n_tiles) ? vt_bytes : 0u;
         const uint8_t *const kb_ = (const uint8_t *)K + (int64_t)kk * D;
+        const int blk = iwave + IW * j; // wave-uniform
+        // K or V^T block chosen by selects, not branches
+        const bool isk = blk < NK;
+        load_lds_16s(isk ? (const void *)kb_ : (const void *)Vt, isk ? k_bytes : v_bytes, voff[j],
+                     isk ? 0u : (uint32_t)kv, isk ? kd + 1024 * blk : vd + 1024 * (blk - NK));
+    };
+    auto issue_batch = [&](int b, lds_char *kd, lds_char *vd) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int blk = wave + kF8Waves * j; // wave-uniform
-            // K or V^T block chosen by selects, not branches
-            const bool isk = blk < NK;
-            load_lds_16s(isk ? (const void *)kb_ : (const void *)Vt, isk ? k_bytes : v_bytes, voff[j],
-                         isk ? 0u : (uint32_t)kv, isk ? kd + 1024 * blk : vd + 1024 * (blk - NK));
-        }
+        for (int j = 0; j < LPI; ++j)
+            load_one(b, kd, vd, j);
     };
 
     // B operand of S^T: lane (r, g) holds q_qi[64 s + 32 g .. + 31]; a negative
@@ -236,7 +251,12 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         return (q0w < N) && (!CAUSAL || t * BC <= q0w + 31);
     };
     // S^T = K Q^T over the head dim in 64-wide steps
-    auto scores = [&](const lds_char *kst) __attribute__((always_inline)) {
+    struct LB_ {
+        int b;
+        lds_char *kd, *vd;
+    };
+    auto scores = [&](const lds_char *kst, LB_ x, int j0, auto nl) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value, NM = DS * KB;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             s[kb] = f32x16{};
@@ -253,6 +273,10 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
                 const i32x8 kv = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 s[kb] = mfma8(kv, qf[st], s[kb]);
+#pragma unroll
+                for (int i = 0; i < NL; ++i)
+                    if (i * NM / NL == st * KB + kb)
+                        load_one(x.b, x.kd, x.vd, j0 + i);
             }
         // kF8Ahead MFMAs' reads ahead, then two reads per MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8Ahead, 0);
@@ -264,7 +288,8 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         __builtin_amdgcn_sched_group_barrier(0x008, kF8Ahead, 0);
     };
     // O^T += V^T P~^T over 64-key steps (blocks 2 s', 2 s' + 1)
-    auto accumulate = [&](const lds_char *vst) __attribute__((always_inline)) {
+    auto accumulate = [&](const lds_char *vst, LB_ x, int j0, auto nl) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value, NM = OB * KB / 2;
         const lds_char *vs = vst + v_lane;
 #pragma unroll
         for (int sp = 0; sp < KB / 2; ++sp)
@@ -279,6 +304,10 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
                                   (int)pk[2 * sp + 1][0], (int)pk[2 * sp + 1][1], (int)pk[2 * sp + 1][2],
                                   (int)pk[2 * sp + 1][3]};
                 o[b] = mfma8(vv, pb, o[b]);
+#pragma unroll
+                for (int i = 0; i < NL; ++i)
+                    if (i * NM / NL == sp * OB + b)
+                        load_one(x.b, x.kd, x.vd, j0 + i);
             }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8Ahead, 0);
 #pragma unroll
@@ -344,11 +373,32 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
         l_run += lt;
     };
     // M(t): O += P~(t-1) V(t-1), then S(t); X(t): softmax of S(t)
+    using z_t = std::integral_constant<int, 0>;
     auto M = [&](int t, const lds_char *vprev, const lds_char *kcur) __attribute__((always_inline)) {
+        const LB_ none{0, nullptr, nullptr};
         if (t >= 1 && t - 1 < n_tiles && active(t - 1))
-            accumulate(vprev);
+            accumulate(vprev, none, 0, z_t{});
         if (t < n_tiles && active(t))
-            scores(kcur);
+            scores(kcur, none, 0, z_t{});
+    };
+    constexpr int LA = LPI / 2;
+    auto ML = [&](int t, const lds_char *vprev, const lds_char *kcur, lds_char *kn, lds_char *vn)
+                  __attribute__((always_inline)) {
+        const LB_ x{t + 1, kn, vn};
+        if (t >= 1 && t - 1 < n_tiles && active(t - 1)) {
+            accumulate(vprev, x, 0, std::integral_constant<int, LA>{});
+        } else {
+#pragma unroll
+            for (int j = 0; j < LA; ++j)
+                load_one(t + 1, kn, vn, j);
+        }
+        if (t < n_tiles && active(t)) {
+            scores(kcur, x, LA, std::integral_constant<int, LPI - LA>{});
+        } else {
+#pragma unroll
+            for (int j = LA; j < LPI; ++j)
+                load_one(t + 1, kn, vn, j);
+        }
     };
     auto X = [&](int t) __attribute__((always_inline)) {
         if (t >= 0 && t < n_tiles && active(t))
@@ -357,24 +407,27 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
 
     // Ping-pong schedule (as in the 16-bit dense kernel): waves 4..7 run one
     // phase behind waves 0..3, so on every SIMD one wave issues MFMAs while
-    // the other does its softmax.  Phase 2c: group 1 issues its half of batch
-    // c + 1 and runs X(c - 1), group 0 runs M(c).  Phase 2c + 1: group 0
-    // issues its half and runs X(c), group 1 M(c); batch c + 1 has landed at
-    // its end (the stages it fills are read by neither phase).
+    // the other does its softmax.  Phase 2c: batch c + 1 goes out (spread:
+    // among group 0's MFMAs; split burst: group 1's share), group 0 runs M(c),
+    // group 1 X(c - 1).  Phase 2c + 1: (split burst: group 0's share goes
+    // out) group 0 runs X(c), group 1 M(c); batch c + 1 has landed at its end
+    // (the stages it fills are read by neither phase).
     const int grp = wave >> 2;
-    issue_batch(0, ks0, vs1);
+    if (!SPREAD || grp == 0)
+        issue_batch(0, ks0, vs1);
     wait_vmcnt<0>();
     tile_barrier();
     if (grp == 0) {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            M(cc, vprev, kcur);
+            if constexpr (SPREAD)
+                ML(cc, vprev, kcur, kn, vn);
+            else
+                M(cc, vprev, kcur);
             tile_barrier();
-            // (group 0 issues its half of batch c + 1 here, at the start of its
-            // softmax phase: at the start of an M phase the loads would stall
-            // the wave, and the matrix core with it, until the address unit
-            // has taken them)
-            if (cc + 1 <= n_tiles)
+            // (split burst: group 0's share of batch c + 1 goes out at the start
+            // of its softmax phase, into stages neither phase reads)
+            if (!SPREAD && cc + 1 <= n_tiles)
                 issue_batch(cc + 1, kn, vn);
             X(cc);
             wait_vmcnt<0>();
@@ -390,7 +443,7 @@ __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     } else {
         auto step = [&](int cc, lds_char *kn, lds_char *vn, const lds_char *vprev, const lds_char *kcur)
                         __attribute__((always_inline)) {
-            if (cc + 1 <= n_tiles)
+            if (!SPREAD && cc + 1 <= n_tiles)
                 issue_batch(cc + 1, kn, vn);
             X(cc - 1);
             tile_barrier();
