@@ -564,12 +564,13 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 
 // ----------------------------------------------------------------------------
 // bf16 / fp16 MFMA kernel, ping-pong schedule ([B, H, N, D] slices, whole or
-// split over keys; head dims with 128-key tiles)
+// split over keys, and packed sequences without the causal mask; head dims
+// with 128-key tiles)
 // ----------------------------------------------------------------------------
 // Same tiles, operand layouts, masking and online softmax as
-// fa_fwd_mfma_kernel; only the order of work differs.  (Packed sequences stay
-// on fa_fwd_mfma_kernel: on their length mix this schedule measured slower.)  A wave's work on key
-// tile t splits into
+// fa_fwd_mfma_kernel; only the order of work differs.  (Causal packed
+// sequences stay on fa_fwd_mfma_kernel: on their length mix this schedule
+// measured slower.)  A wave's work on key tile t splits into
 //   M(t): O += P(t-1) V(t-1), then S(t) = K(t) Q^T   (MFMA, LDS reads)
 //   X(t): mask and online softmax of S(t) into P(t)   (VALU)
 // and every wave runs M(0) X(0) M(1) X(1) ... M(T), one item per phase, with
@@ -596,10 +597,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 // tiles before O / l is rounded and stored.
 template <typename E, int D, bool CAUSAL, int MODE, int KG>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs a) {
-    constexpr bool SPLIT = MODE == kSplit;
+    constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
     using Cfg = MfmaCfg<D>;
     static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
-    static_assert(MODE != kVarlen, "square [B, H, N, D] slices only");
     static_assert(KG == 1 || ((KG == 2 || KG == 4) && MODE == kDense), "key groups of whole slices");
     constexpr int W = Cfg::WAVES, BC = Cfg::BC;
     constexpr int BCS = BC / KG;         // keys of a wave's share of a tile
@@ -627,17 +627,63 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int g = lane >> 5;
 
     // --- slice, query block, key range ----------------------------------------
-    const SliceBlock blk = slice_block<D, MODE, CAUSAL, KG>(a, wave);
-    if (split_block_empty<D, MODE>(blk, a, tid))
-        return;
+    // Square slices: a (slice, query block) of [B, H, N, D] (and for a key split
+    // the split's keys).  Packed sequences: a (sequence, head) grid row with
+    // its own query and key counts Nq, Nk (causal: query i sees keys
+    // j <= i + coff, coff = Nk - Nq, bottom-right aligned).
+    SliceBlock blk;
+    int Nq, Nk, coff, n_act_w = 0;
+    int64_t q_off, k_off, lse_off;
+    if constexpr (VARLEN) {
+        const Work wk = map_workgroup_strided(blockIdx.x, gridDim.x, a.n_qblk, CAUSAL);
+        const SeqSlice sq = seq_slice(a, wk.bh, D);
+        Nq = sq.nq;
+        Nk = sq.nk;
+        coff = Nk - Nq;
+        q_off = sq.q_off;
+        k_off = sq.k_off;
+        lse_off = sq.lse_off;
+        blk.bh = wk.bh;
+        blk.split = 0;
+        blk.q0 = wk.qb * QBLK;
+        blk.q0w = blk.q0 + 32 * wave;
+        blk.k_begin = 0;
+        if (blk.q0 >= Nq) // the grid covers the longest sequence
+            return;
+        blk.kv_end = CAUSAL ? min(Nk, blk.q0 + QBLK + coff) : Nk;
+        blk.n_tiles = blk.kv_end > 0 ? (blk.kv_end + BC - 1) / BC : 0;
+        if (blk.n_tiles == 0) { // no key is visible to any row of the block: O = 0, lse = -inf
+            if (tid < QBLK && blk.q0 + tid < Nq) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                uint16_t *__restrict__ Oz = (uint16_t *)a.o + q_off + (int64_t)(blk.q0 + tid) * D;
+#pragma unroll
+                for (int c = 0; c < D / 8; ++c)
+                    *(u32x4 *)(Oz + 8 * c) = z;
+                a.lse[lse_off + blk.q0 + tid] = -INFINITY;
+            }
+            return;
+        }
+        // causal: tiles t < n_act_w hold a key this wave's rows can see
+        const int last_w = blk.q0w + 31 + coff;
+        n_act_w = last_w < 0 ? 0 : last_w / BC + 1;
+    } else {
+        blk = slice_block<D, MODE, CAUSAL, KG>(a, wave);
+        if (split_block_empty<D, MODE>(blk, a, tid))
+            return;
+        Nq = a.N;
+        Nk = a.N;
+        coff = 0;
+        q_off = (int64_t)blk.bh * a.N * D;
+        k_off = q_off;
+        lse_off = (int64_t)blk.bh * a.N;
+    }
     const int kws = (wave % KG) * BCS; // the wave's keys inside a tile
-    const int N = a.N;
-    const int64_t off = (int64_t)blk.bh * N * D;
-    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + off;
-    const uint16_t *__restrict__ K = (const uint16_t *)a.k + off;
-    const uint16_t *__restrict__ V = (const uint16_t *)a.v + off;
-    uint16_t *__restrict__ O = (uint16_t *)a.o + off;
-    float *__restrict__ LSE = a.lse + (int64_t)blk.bh * N;
+    const int N = Nk;                  // (square slices: Nq = Nk = N)
+    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + q_off;
+    const uint16_t *__restrict__ K = (const uint16_t *)a.k + k_off;
+    const uint16_t *__restrict__ V = (const uint16_t *)a.v + k_off;
+    uint16_t *__restrict__ O = (uint16_t *)a.o + q_off;
+    float *__restrict__ LSE = a.lse + lse_off;
     const int q0w = blk.q0w; // first query row of this wave
     const int qi = q0w + r;  // this lane's query row
     // (k_begin is 0 unless split; stated so, the compiler keeps the register
@@ -702,7 +748,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     const int v_lane = (g + 2 * ((lane >> 2) & 3)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
     u32x4 qf[DC];
-    load_q<D>(qf, Q, qi, N, g, a.qneg);
+    load_q<D>(qf, Q, qi, Nq, g, a.qneg);
     f32x16 o[OB];
 #pragma unroll
     for (int b = 0; b < OB; ++b)
@@ -717,7 +763,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     // (written separately for whole-tile waves: stated through kws the dense
     // causal instances spill)
     auto active = [&](int t) __attribute__((always_inline)) {
-        if constexpr (KG == 1) {
+        if constexpr (VARLEN) {
+            return (q0w < Nq) && (!CAUSAL || t < n_act_w);
+        } else if constexpr (KG == 1) {
             return (q0w < N) && (!CAUSAL || k_begin + t * BC <= q0w + 31);
         } else {
             const int k0 = k_begin + t * BC + kws;
@@ -800,8 +848,12 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     auto softmax = [&](int t) __attribute__((always_inline)) {
         const int k0 = k_begin + t * BC + kws;
         // masking: keys beyond N, and keys after the query when causal
-        if ((k0 + BCS > N) || (CAUSAL && k0 + BCS - 1 > q0w))
+        if constexpr (VARLEN) {
+            if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + coff))
+                mask_below<KB>(s, (CAUSAL ? min(Nk, qi + coff + 1) : Nk) - k0 - g);
+        } else if ((k0 + BCS > N) || (CAUSAL && k0 + BCS - 1 > q0w)) {
             mask_keys<KB, CAUSAL>(s, k0, N, qi, 0, g);
+        }
         online_softmax<E, KB, OB>(s, pk, o, m_run, l_run, c);
     };
     using none_t = std::integral_constant<int, 0>;
@@ -956,7 +1008,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
         return;
     }
     static_assert(2 * 32 * OP <= KBYTES, "two waves' O rows fit in a stage array");
-    store_o<E, D>(o, 1.0f / l_tot, m_run, l_tot, own + (wave & 1) * 32 * OP, O, LSE, q0w, N, lane);
+    // (packed sequences: a row that sees no key has l = 0 and gets O = 0, lse = -inf)
+    const float inv = (VARLEN && !(l_tot > 0.f)) ? 0.f : 1.0f / l_tot;
+    store_o<E, D>(o, inv, m_run, l_tot, own + (wave & 1) * 32 * OP, O, LSE, q0w, Nq, lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -1312,7 +1366,13 @@ template <typename E, int D, int MODE>
 hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream, int kg) {
     // the tile stages are static LDS (MfmaCfg<D>::LDS bytes); no dynamic LDS
     constexpr int T = MfmaCfg<D>::THREADS;
-    if constexpr (MODE != kVarlen && MfmaCfg<D>::PINGPONG) {
+    if constexpr (MODE == kVarlen && MfmaCfg<D>::PINGPONG) {
+        // packed sequences: the ping-pong kernel without the causal mask; causal
+        // ones stay on the one-barrier kernel, which measured faster on them
+        if (!causal)
+            return launch<fa_fwd_pp_kernel<E, D, false, MODE, 1>, T>(nwg, 0, args, stream);
+        return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
+    } else if constexpr (MfmaCfg<D>::PINGPONG) {
         if constexpr (MODE == kDense) {
             if (kg == 4)
                 return launch_pp<E, D, MODE, 4>(causal, nwg, args, stream);
@@ -1403,7 +1463,7 @@ const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg)
                             if (t == 0)
                                 snprintf(out, 96, "fa_fwd_f32_kernel<%d, %s, %d, %d>", d, cs, m,
                                          m == kDense ? g : 1);
-                            else if (m != kVarlen && d <= 128)
+                            else if (d <= 128 && (m != kVarlen || !c))
                                 snprintf(out, 96, "fa_fwd_pp_kernel<%s, %d, %s, %d, %d>", e, d, cs, m,
                                          m == kDense ? g : 1);
                             else
