@@ -77,9 +77,21 @@ __device__ __forceinline__ int tr_lane(int lane, int P) {
     return ((lane >> 5) + 2 * ((lane >> 2) & 3)) * P + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
+// LDS layout of a tile read both ways (b128 operand reads of 16 rows at one
+// column, transposing reads of rows 2e + g at two column halves): row pitch
+// P = 2D + 32 bytes, and rows with bit 3 set start 16 bytes into their slot.
+// The 16 rows a b128 read touches then fall in 16 distinct 16-byte bank slots
+// (P / 16 is even: rows 0..7 take the even slots, the shifted rows 8..15 the
+// odd ones), and the four rows 2e + g of a transposing read, at both column
+// halves, in eight distinct 32-byte bank ranges (2P = 64 or 192 mod 256).
+__device__ __forceinline__ constexpr int row_shift(int row) { return ((row >> 3) & 1) * 16; }
+
+// the lo read covers rows g + 2e (no shift), the hi read the same rows 8 on
+// (shifted)
 __device__ __forceinline__ u32x4 tr_read(const lds_char *p, int P) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p + 8 * P));
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p + 8 * P + 16));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
     const u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
@@ -97,10 +109,12 @@ __device__ __forceinline__ void load_lds_4(const void *base, uint32_t bytes, uin
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
-// Two R-row tiles X and Y (D 16-bit columns, row pitch P bytes) of one LDS
-// stage, filled by W waves with direct-to-LDS loads: load j of wave w fills
-// the 1 KB block w + W j; blocks [0, NX) hold X, [NX, 2 NX) Y, the rest are
-// spare (they re-read X's first row).  Every wave issues LPW loads per tile.
+// Two R-row tiles X and Y (D 16-bit columns, row pitch P bytes, rows with
+// bit 3 set shifted by 16 bytes) of one LDS stage, filled by W waves with
+// direct-to-LDS loads: load j of wave w fills the 1 KB block w + W j; blocks
+// [0, NX) hold X, [NX, 2 NX) Y, the rest are spare (they re-read X's first
+// row, as do the slots of a row's padding).  Every wave issues LPW loads per
+// tile.
 template <int W, int R, int D, int P>
 struct TilePair {
     static constexpr int NX = R * P / 1024;
@@ -119,8 +133,10 @@ struct TilePair {
             const int blk = wave + W * j;
             const bool used = blk < 2 * NX;
             const int pos = 1024 * (blk < NX ? blk : blk - NX) + 16 * lane;
-            const int chunk = (pos % P) / 16;
-            const uint32_t off = used ? (uint32_t)((pos / P) * D + (chunk < D / 8 ? 8 * chunk : 0)) * 2u : 0u;
+            const int row = pos / P, o = pos % P - row_shift(row);
+            const int chunk = o / 16;
+            const bool data = o >= 0 && chunk < D / 8;
+            const uint32_t off = used ? (uint32_t)(row * D + (data ? 8 * chunk : 0)) * 2u : 0u;
             voff2[j / 2] |= off << (16 * (j % 2));
         }
     }
@@ -187,7 +203,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t *__res
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
     constexpr int W = 8, BC = 64, KB = BC / 32, DC = D / 16, OB = D / 32;
-    constexpr int P = 2 * D + 16; // K and V row pitch (bytes)
+    constexpr int P = 2 * D + 32; // K and V row pitch (bytes; rows with bit 3 set shifted by 16)
     constexpr int OP = 2 * D + 16; // dQ staging pitch
     using Tiles = TilePair<W, BC, D, P>;
     __shared__ __attribute__((aligned(16))) char stage0_raw[Tiles::BYTES];
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
     Tiles tiles;
     tiles.init(wave, lane);
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    const int k_lane = perm_row(r) * P + 16 * g;
+    const int k_lane = perm_row(r) * P + row_shift(perm_row(r)) + 16 * g;
     const int t_lane = tr_lane(lane, P);
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: lane (r, g) holds
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
 template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int W = 4, BK = 32 * W, TQ = 64, QB = TQ / 32, DC = D / 16, OB = D / 32;
-    constexpr int P = 2 * D + 16; // Q and dO row pitch (bytes)
+    constexpr int P = 2 * D + 32; // Q and dO row pitch (bytes; rows with bit 3 set shifted by 16)
     constexpr int OP = 2 * D + 16; // dK / dV staging pitch
     using Tiles = TilePair<W, TQ, D, P>;
     // per stage: the Q and dO tiles, then lse (64 floats), Delta (64 floats) and
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             issue_one(t, st, j);
     };
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    const int q_lane = perm_row(r) * P + 16 * g;
+    const int q_lane = perm_row(r) * P + row_shift(perm_row(r)) + 16 * g;
     const int t_lane = tr_lane(lane, P);
 
     // B operands of S = Q K^T and dP = dO V^T: lane (r, g) holds
