@@ -12,16 +12,23 @@
 //
 // Three kernels on one stream:
 //   fa_bwd_delta_kernel  Delta = rowsum(dO * O) in fp32 (memory-bound);
-//   fa_bwd_dq_kernel     one workgroup per 256 query rows (8 waves x 32 rows),
-//                        looping over 64-key tiles of K and V: S^T = K Q^T,
+//   fa_bwd_dq_kernel     one workgroup per 256 query rows (8 waves x 32 rows;
+//                        4 waves and 128 rows at D > 128, where a wave's
+//                        operands and accumulators need a SIMD's whole
+//                        register file), looping over 64-key tiles of K and
+//                        V: S^T = K Q^T,
 //                        dP^T = V dO^T, dS, then dQ^T += K^T dS^T, the tile's
 //                        two 32-key halves staggered as in the dK/dV kernel;
 //   fa_bwd_dkdv_kernel   one workgroup per 128 keys (4 waves x 32 keys), looping
 //                        over 64-query tiles of Q and dO: S = Q K^T, dP = dO V^T,
-//                        dS, then dV^T += dO^T P and dK^T += Q^T dS.
+//                        dS, then dV^T += dO^T P and dK^T += Q^T dS.  At D = 256
+//                        the two accumulators, K and V do not fit one wave's
+//                        registers together: one launch accumulates dV (S and
+//                        dV^T only), a second dK (S, dP and dK^T).
 // Two kernels recompute S and dP (seven contractions per tile pair instead of
-// five), so that every output is written exactly once by one workgroup: no
-// atomics, no fp32 accumulation buffer, results independent of scheduling.
+// five; eight at D = 256), so that every output is written exactly once by one
+// workgroup: no atomics, no fp32 accumulation buffer, results independent of
+// scheduling.
 //
 // MFMA layouts follow the forward kernel.  In the dQ kernel a lane pair owns
 // a query (the accumulator column); accumulator entry i of lane half g is key
@@ -169,8 +176,8 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                            const uint16_t *__restrict__ dO,
                                                            float *__restrict__ delta, int64_t rows) {
-    constexpr int TPR = delta_lanes(D); // lanes per row (8, 4 or 16)
-    constexpr int CPL = D / 8 / TPR;    // 16-byte chunks per lane (1, 3 or 1)
+    constexpr int TPR = delta_lanes(D); // lanes per row (D 64..256: 8, 4, 16, 8, 32)
+    constexpr int CPL = D / 8 / TPR;    // 16-byte chunks per lane (1, 3, 1, 3, 1)
     const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = item / TPR;
     const int c = (int)(item % TPR);
@@ -198,11 +205,15 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t *__res
 }
 
 // ----------------------------------------------------------------------------
-// dQ: 256 query rows per workgroup, 64-key tiles
+// dQ: 32 query rows per wave, 64-key tiles
 // ----------------------------------------------------------------------------
+// Waves per dQ workgroup: 8 (two per SIMD) while a wave's Q and dO operands
+// and dQ accumulator fit half the register file, else 4.
+constexpr int dq_waves(int D) { return D > 128 ? 4 : 8; }
+
 template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
-    constexpr int W = 8, BC = 64, KB = BC / 32, DC = D / 16, OB = D / 32;
+__global__ __launch_bounds__(64 * dq_waves(D)) void fa_bwd_dq_kernel(BwdArgs a) {
+    constexpr int W = dq_waves(D), QR = 32 * W, BC = 64, KB = BC / 32, DC = D / 16, OB = D / 32;
     constexpr int P = 2 * D + 32; // K and V row pitch (bytes; rows with bit 3 set shifted by 16)
     constexpr int OP = 2 * D + 16; // dQ staging pitch
     using Tiles = TilePair<W, BC, D, P>;
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
     const int r = lane & 31;
     const int g = lane >> 5;
     const int N = a.N;
-    const int n_qblk = (N + 255) / 256;
+    const int n_qblk = (N + QR - 1) / QR;
     const Blk wk = map_bwd(blockIdx.x, gridDim.x, n_qblk, CAUSAL);
     const int64_t slice = (int64_t)wk.bh * N * D;
     const uint16_t *__restrict__ Q = (const uint16_t *)a.q + slice;
@@ -226,10 +237,10 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
     const uint16_t *__restrict__ dO = (const uint16_t *)a.dout + slice;
     uint16_t *__restrict__ dQ = (uint16_t *)a.dq + slice;
 
-    const int q0 = wk.blk * 256;
+    const int q0 = wk.blk * QR;
     const int q0w = q0 + 32 * wave;
     const int qi = q0w + r;
-    const int kv_end = CAUSAL ? min(N, q0 + 256) : N;
+    const int kv_end = CAUSAL ? min(N, q0 + QR) : N;
     const int n_tiles = (kv_end + BC - 1) / BC;
 
     Tiles tiles;
@@ -397,9 +408,19 @@ __global__ __launch_bounds__(512) void fa_bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------
 // dK, dV: 128 keys per workgroup (4 waves x 32), 64-query tiles
 // ----------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL>
+// Which key gradients one launch of the dK/dV kernel accumulates.
+enum KeyGrads { kDkDv = 0, kDvOnly = 1, kDkOnly = 2 };
+// D = 256: the dV^T and dK^T accumulators (256 registers per lane) with the K
+// and V rows (128) and the S / dP tiles exceed a SIMD's 512 registers, so dV
+// and dK take a launch each (dV needs neither V nor dP).
+constexpr bool split_key_grads(int D) { return D > 192; }
+
+template <typename E, int D, bool CAUSAL, int PART>
 __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int W = 4, BK = 32 * W, TQ = 64, QB = TQ / 32, DC = D / 16, OB = D / 32;
+    constexpr bool DV = PART != kDkOnly, DK = PART != kDvOnly; // accumulated here
+    // MFMAs per 32-query half: S (and dP), then dV^T / dK^T
+    constexpr int NSD = (DK ? 2 : 1) * DC, NGR = ((DV ? 1 : 0) + (DK ? 1 : 0)) * 2 * OB;
     constexpr int P = 2 * D + 32; // Q and dO row pitch (bytes; rows with bit 3 set shifted by 16)
     constexpr int OP = 2 * D + 16; // dK / dV staging pitch
     using Tiles = TilePair<W, TQ, D, P>;
@@ -466,19 +487,22 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
 
     // B operands of S = Q K^T and dP = dO V^T: lane (r, g) holds
     // k_kj[16c + 8g ..] and v_kj[16c + 8g ..]
-    u32x4 kf[DC], vf[DC];
+    u32x4 kf[DC], vf[DK ? DC : 1];
 #pragma unroll
     for (int cc = 0; cc < DC; ++cc) {
         kf[cc] = kj < N ? *(const u32x4 *)(K + (int64_t)kj * D + 16 * cc + 8 * g) : zero4;
-        vf[cc] = kj < N ? *(const u32x4 *)(V + (int64_t)kj * D + 16 * cc + 8 * g) : zero4;
+        if constexpr (DK)
+            vf[cc] = kj < N ? *(const u32x4 *)(V + (int64_t)kj * D + 16 * cc + 8 * g) : zero4;
     }
     const float c2 = a.c2;
 
-    f32x16 dva[OB], dka[OB];
+    f32x16 dva[DV ? OB : 1], dka[DK ? OB : 1];
 #pragma unroll
     for (int b = 0; b < OB; ++b) {
-        dva[b] = f32x16{};
-        dka[b] = f32x16{};
+        if constexpr (DV)
+            dva[b] = f32x16{};
+        if constexpr (DK)
+            dka[b] = f32x16{};
     }
 
     // One 64-query tile in two 32-query halves, staggered so that a half's
@@ -492,15 +516,17 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
         if (active) {
             const lds_char *qs = cur + q_lane;
             const lds_char *ds = cur + Tiles::NX * 1024 + q_lane;
-            f32x16 s[QB], dp[QB];
+            f32x16 s[QB], dp[DK ? QB : 1];
             // S = Q K^T and dP = dO V^T for query half qb
             auto sdp = [&](int qb) __attribute__((always_inline)) {
                 s[qb] = f32x16{};
-                dp[qb] = f32x16{};
+                if constexpr (DK)
+                    dp[qb] = f32x16{};
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc) {
                     s[qb] = E::mfma(lds_u32x4(qs + 32 * qb * P + 32 * cc), kf[cc], s[qb]);
-                    dp[qb] = E::mfma(lds_u32x4(ds + 32 * qb * P + 32 * cc), vf[cc], dp[qb]);
+                    if constexpr (DK)
+                        dp[qb] = E::mfma(lds_u32x4(ds + 32 * qb * P + 32 * cc), vf[cc], dp[qb]);
                 }
             };
             // P = exp2(c2 s - log2(e) lse_i), dS = P (dP - Delta_i); causal: a query
@@ -509,12 +535,14 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             const bool diag = CAUSAL && i0 < k0w + 31;
             const int lim = kj - i0 - g; // entry (qb, i) is query i0 + 32 qb + 2 i + g
             const lds_char *stat = cur + STAT + 64 * g;
-            uint32_t pp[QB][8], pd[QB][8];
+            uint32_t pp[DV ? QB : 1][8], pd[DK ? QB : 1][8];
             auto soft = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 128 * qb + 16 * m);
-                    const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 256 + 128 * qb + 16 * m);
+                    f32x4 d4 = {};
+                    if constexpr (DK)
+                        d4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 256 + 128 * qb + 16 * m);
                     float pv[4], sv[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -523,12 +551,17 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
                         if (diag)
                             p = (32 * qb + 2 * i >= lim) ? p : 0.f;
                         pv[u] = p;
-                        sv[u] = p * (dp[qb][i] - d4[u]);
+                        if constexpr (DK)
+                            sv[u] = p * (dp[qb][i] - d4[u]);
                     }
-                    pp[qb][2 * m] = E::pack(pv[0], pv[1]);
-                    pp[qb][2 * m + 1] = E::pack(pv[2], pv[3]);
-                    pd[qb][2 * m] = E::pack(sv[0], sv[1]);
-                    pd[qb][2 * m + 1] = E::pack(sv[2], sv[3]);
+                    if constexpr (DV) {
+                        pp[qb][2 * m] = E::pack(pv[0], pv[1]);
+                        pp[qb][2 * m + 1] = E::pack(pv[2], pv[3]);
+                    }
+                    if constexpr (DK) {
+                        pd[qb][2 * m] = E::pack(sv[0], sv[1]);
+                        pd[qb][2 * m + 1] = E::pack(sv[2], sv[3]);
+                    }
                 }
             };
             // dV^T += dO^T P and dK^T += Q^T dS for query half qb
@@ -540,10 +573,16 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int mm = 0; mm < 2; ++mm) {
                         const int off = (32 * qb + 16 * mm) * P + 64 * b;
-                        const u32x4 pv = {pp[qb][4 * mm], pp[qb][4 * mm + 1], pp[qb][4 * mm + 2], pp[qb][4 * mm + 3]};
-                        const u32x4 sv = {pd[qb][4 * mm], pd[qb][4 * mm + 1], pd[qb][4 * mm + 2], pd[qb][4 * mm + 3]};
-                        dva[b] = E::mfma(tr_read(dt + off, P), pv, dva[b]);
-                        dka[b] = E::mfma(tr_read(qt + off, P), sv, dka[b]);
+                        if constexpr (DV) {
+                            const u32x4 pv = {pp[qb][4 * mm], pp[qb][4 * mm + 1], pp[qb][4 * mm + 2],
+                                              pp[qb][4 * mm + 3]};
+                            dva[b] = E::mfma(tr_read(dt + off, P), pv, dva[b]);
+                        }
+                        if constexpr (DK) {
+                            const u32x4 sv = {pd[qb][4 * mm], pd[qb][4 * mm + 1], pd[qb][4 * mm + 2],
+                                              pd[qb][4 * mm + 3]};
+                            dka[b] = E::mfma(tr_read(qt + off, P), sv, dka[b]);
+                        }
                     }
             };
             // MFMAs of one half with the softmax VALU work of the other in
@@ -563,7 +602,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             // one after each (issued back to back they stall the wave, and with
             // one wave per SIMD the matrix core with it); at D = 64 the last
             // ones go among the next section's MFMAs, one after every other
-            constexpr int L0 = (2 * DC - 4) < NLD ? (2 * DC - 4) : NLD;
+            constexpr int L0 = (NSD - 4) < NLD ? (NSD - 4) : NLD;
             sdp(0);
 #pragma unroll
             for (int j = 0; j < L0; ++j)
@@ -571,7 +610,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             // four operand reads ahead of the first half's S / dP MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int n = 0; n < 2 * DC - 4; ++n) {
+            for (int n = 0; n < NSD - 4; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if (n < L0)
@@ -585,7 +624,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             for (int j = L0; j < NLD; ++j)
                 issue_one(t + 1, next, j);
             {
-                constexpr int NM = 2 * DC, RP = 1, L1 = NLD - L0;
+                constexpr int NM = NSD, RP = 1, L1 = NLD - L0;
                 __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
                 for (int n = 0; n < NM; ++n) {
@@ -599,14 +638,14 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             grad(0);
             soft(1);
-            interleave(std::integral_constant<int, 4 * OB>{}, std::integral_constant<int, 2>{});
+            interleave(std::integral_constant<int, NGR>{}, std::integral_constant<int, 2>{});
             __builtin_amdgcn_sched_barrier(0);
             grad(1);
             // eight transposing reads (four MFMAs) ahead of the second half's
             // dV / dK MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int n = 0; n < 4 * OB - 4; ++n) {
+            for (int n = 0; n < NGR - 4; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
@@ -636,14 +675,14 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
     lds_char *ow = (wave < 2 ? stage0 : stage1) + (wave & 1) * 32 * OP;
     const float sc = a.scale;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = DV ? 0 : 1; pass < (DK ? 2 : 1); ++pass) {
         uint16_t *__restrict__ OUT = pass == 0 ? dV : dK;
         if (k0w < N) {
 #pragma unroll
             for (int b = 0; b < OB; ++b)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
-                    const f32x16 &x = pass == 0 ? dva[b] : dka[b];
+                    const f32x16 &x = pass == 0 ? dva[DV ? b : 0] : dka[DK ? b : 0];
                     const float f = pass == 0 ? 1.f : sc;
                     const u32x2 w = {E::pack(x[4 * a4] * f, x[4 * a4 + 1] * f),
                                      E::pack(x[4 * a4 + 2] * f, x[4 * a4 + 3] * f)};
@@ -675,14 +714,27 @@ hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const int64_t n_q = BH * ((args.N + 255) / 256);
+    constexpr int WQ = dq_waves(D);
+    const int64_t n_q = BH * ((args.N + 32 * WQ - 1) / (32 * WQ));
     const int64_t n_k = BH * ((args.N + 127) / 128);
+    auto key_grads = [&](auto causal_c) {
+        constexpr bool C = decltype(causal_c)::value;
+        if constexpr (split_key_grads(D)) {
+            hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, C, kDvOnly>), dim3((unsigned)n_k), dim3(256), 0, stream,
+                               args);
+            hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, C, kDkOnly>), dim3((unsigned)n_k), dim3(256), 0, stream,
+                               args);
+        } else {
+            hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, C, kDkDv>), dim3((unsigned)n_k), dim3(256), 0, stream,
+                               args);
+        }
+    };
     if (causal) {
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, true>), dim3((unsigned)n_q), dim3(512), 0, stream, args);
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, true>), dim3((unsigned)n_k), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, true>), dim3((unsigned)n_q), dim3(64 * WQ), 0, stream, args);
+        key_grads(std::true_type{});
     } else {
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, false>), dim3((unsigned)n_q), dim3(512), 0, stream, args);
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, false>), dim3((unsigned)n_k), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, false>), dim3((unsigned)n_q), dim3(64 * WQ), 0, stream, args);
+        key_grads(std::false_type{});
     }
     return hipGetLastError();
 }
@@ -695,6 +747,10 @@ hipError_t launch_bwd_e(int D, bool causal, int64_t BH, const BwdArgs &args, hip
         return launch_bwd_t<E, 64>(causal, BH, args, stream);
     if (D == 96)
         return launch_bwd_t<E, 96>(causal, BH, args, stream);
+    if (D == 192)
+        return launch_bwd_t<E, 192>(causal, BH, args, stream);
+    if (D == 256)
+        return launch_bwd_t<E, 256>(causal, BH, args, stream);
     return launch_bwd_t<E, 128>(causal, BH, args, stream);
 }
 

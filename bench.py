@@ -332,16 +332,18 @@ def bench_varlen(name, steps, warmup):
 
 
 def bench_bwd(name, steps, warmup):
-    """fa_bwd on the headline shape, or at D = 96 for "bwd_d96*" (stderr line
-    only).  FLOPs: the five contractions of the backward pass, 10*B*H*N^2*D
-    (2.5x the forward's count, halved for causal); the kernels recompute S and
-    dP once more (seven)."""
+    """fa_bwd on the headline shape, at D = 96 for "bwd_d96*", or B4 H8 N4096
+    at D = 192 / 256 for "bwd_d192*" / "bwd_d256*" (stderr line only).  FLOPs:
+    the five contractions of the backward pass, 10*B*H*N^2*D (2.5x the
+    forward's count, halved for causal); the kernels recompute S and dP once
+    more (seven; eight at D = 256)."""
     import torch
 
     import attention_fa_fwd_02_amd as fa
     import fa_inputs as fi
     causal = name.endswith("causal")
-    B, H, N, D, dtype = 4, 16, 4096, 96 if name.startswith("bwd_d96") else 128, "bf16"
+    D = int(name[5:].split("_")[0]) if name.startswith("bwd_d") else 128
+    B, H, N, dtype = 4, (8 if D > 128 else 16), 4096, "bf16"
     host, (q, k, v) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0))
     _, (do, _, _) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0), seed=1004 + 7919)
     scale = 1.0 / math.sqrt(D)
@@ -472,7 +474,8 @@ def main():
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), warm_seconds=0.5)
         for name in ("varlen", "varlen_causal"):
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal"):
+        for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
+                     "bwd_d256_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("fp8", "fp8_causal", "fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))

@@ -361,7 +361,7 @@ uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
 
 /*
  * fa_bwd -- enqueue the backward pass on `stream` (three kernels: Delta, dQ,
- * dK/dV).
+ * dK/dV; at D = 256 dV and dK are two launches of the last).
  *
  *   q, k, v, o, dout  device pointers, [B, H, N, D] of element type `dtype`,
  *                     read-only: the forward inputs, its output O and the
@@ -381,7 +381,7 @@ uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  * scale, causal not 0/1, an unknown dtype, a tensor or the workspace not
  * 16-byte aligned, lse not 4-byte aligned, workspace_bytes too small, or
  * dq/dk/dv/workspace overlapping each other or any input;
- * FA_ERR_UNSUPPORTED for fp32, D other than 64/96/128, the size limits of
+ * FA_ERR_UNSUPPORTED for fp32, D other than 64/96/128/192/256, the size limits of
  * fa_fwd, B*H*ceil(N/128) >= 2^23, or a device that is not gfx950;
  * FA_ERR_HIP when a device query or a launch fails.  All checks precede any
  * HIP call; the library allocates nothing.  Every output is written by

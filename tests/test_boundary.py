@@ -396,7 +396,7 @@ def test_bwd_workspace_bytes():
 def test_bwd_good_arguments_pass():
     assert bcheck() == fa.FA_OK and bcheck(arch=None) == fa.FA_OK
     for dt in (1, 2):
-        for D in (64, 96, 128):
+        for D in (64, 96, 128, 192, 256):
             for c in (0, 1):
                 assert bcheck(dtype=dt, D=D, causal=c) == fa.FA_OK
     assert bcheck(scale=0.0) == fa.FA_OK and bcheck(scale=-2.0) == fa.FA_OK
@@ -412,7 +412,7 @@ def test_bwd_invalid_arguments(kw):
     assert bcheck(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=0), dict(D=80), dict(D=192), dict(D=256), dict(N=1 << 30),
+@pytest.mark.parametrize("kw", [dict(dtype=0), dict(D=80), dict(D=160), dict(D=512), dict(N=1 << 30),
                                 dict(B=1 << 14, H=1 << 6, N=128 * 8, wsb=1 << 62)])
 def test_bwd_unsupported(kw):
     assert bcheck(**kw) == fa.FA_ERR_UNSUPPORTED

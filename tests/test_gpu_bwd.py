@@ -118,7 +118,7 @@ def term_magnitudes(q, k, v, do, sc, causal, o_dev):
 
 
 @pytest.mark.parametrize("N", [1, 31, 64, 100, 255, 257, 600])
-@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ragged(N, D, dtype, causal):
@@ -129,6 +129,14 @@ def test_bwd_ragged(N, D, dtype, causal):
 def test_bwd_d96_several_blocks(causal):
     """D = 96 over several query and key blocks with a ragged tail (N = 1100)."""
     check_bwd(1, 3, 1100, 96, "bf16", causal, seed=796)
+
+
+@pytest.mark.parametrize("D", [192, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_wide_heads_several_blocks(D, causal):
+    """D = 192 and 256 (dQ in 128-row blocks; at 256 dV and dK from separate
+    launches) over several query and key blocks with a ragged tail (N = 700)."""
+    check_bwd(1, 2, 700, D, "bf16", causal, seed=1920 + D)
 
 
 @pytest.mark.parametrize("causal", [False, True])
