@@ -394,7 +394,8 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: fl
 
 def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False, stream=None):
     """(dQ, dK, dV) of the forward pass that produced o and lse (fa_bwd); all
-    [B, H, N, D] CUDA tensors of one 16-bit dtype, lse float32 [B, H, N]."""
+    [B, H, N, D] CUDA tensors of one dtype (bfloat16, float16, or float32 at
+    D = 64 / 128), lse float32 [B, H, N]."""
     import torch
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must all be [B, H, N, D] with the same shape")

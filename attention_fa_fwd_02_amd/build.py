@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
            os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_bwd_f32.hip"),
            os.path.join(CSRC, "fa_fp8.hip"), os.path.join(CSRC, "fa_static.hip")]
 HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_fwd_common.h"),
            os.path.join(ROOT, "include", "fa.h")]

@@ -136,8 +136,8 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32), fp32 "
-               "backward, problem too large for "
+        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32), "
+               "problem too large for "
                "one launch, too many "
                "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
                "device is not gfx950)";
@@ -451,7 +451,7 @@ fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (dtype == FA_DTYPE_F32 || (D != 64 && D != 96 && D != 128 && D != 192 && D != 256))
+    if (dtype == FA_DTYPE_F32 ? (D != 64 && D != 128) : (D != 64 && D != 96 && D != 128 && D != 192 && D != 256))
         return FA_ERR_UNSUPPORTED;
     // B, H < 2^31 keep B * H (< 2^62) exact; the products are then compared
     // against their limits without being formed

@@ -47,28 +47,6 @@
 namespace fa {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
-// Workgroups go round-robin over the 8 XCDs (id % 8); with a grid that is a
-// multiple of 8, XCD x takes the contiguous logical range [x n/8, (x+1) n/8),
-// so the blocks of one (batch, head) slice share an L2.  `reverse` hands the
-// blocks of a slice out last index first.
-struct Blk {
-    int bh;
-    int blk;
-};
-__device__ __forceinline__ Blk map_bwd(int wg, int nwg, int n_blk, bool reverse) {
-    int L = wg;
-    if ((nwg & 7) == 0)
-        L = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    Blk b;
-    b.bh = L / n_blk;
-    b.blk = L - b.bh * n_blk;
-    if (reverse)
-        b.blk = n_blk - 1 - b.blk;
-    return b;
-}
-
 // Row order inside a 32-row MFMA A-operand block read from LDS: MFMA row r is
 // tile row 8(r/8) + 2(r%4) + (r/4)%2, so accumulator entry i of lane half g
 // is tile row 2i + g.
@@ -107,13 +85,6 @@ __device__ __forceinline__ u32x4 tr_read(const lds_char *p, int P) {
 
 __device__ __forceinline__ u32x4 lds_u32x4(const lds_char *p) {
     return *(const __attribute__((address_space(3))) u32x4 *)p;
-}
-
-// Direct global -> LDS load of 4 bytes per lane (lane l writes lds + 4 l).
-__device__ __forceinline__ void load_lds_4(const void *base, uint32_t bytes, uint32_t voff, lds_char *lds) {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
 // Two R-row tiles X and Y (D 16-bit columns, row pitch P bytes, rows with
@@ -755,6 +726,8 @@ hipError_t launch_bwd_e(int D, bool causal, int64_t BH, const BwdArgs &args, hip
 }
 
 hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
+    if (dtype == 0)
+        return launch_bwd_f32(D, causal, BH, args, stream);
     if (dtype == 1)
         return launch_bwd_e<Bf16>(D, causal, BH, args, stream);
     return launch_bwd_e<F16>(D, causal, BH, args, stream);

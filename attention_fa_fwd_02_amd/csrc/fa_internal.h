@@ -106,6 +106,8 @@ struct BwdArgs {
 // problem; arguments are already validated.
 hipError_t launch_bwd(int dtype, int D, bool causal, int64_t BH, const BwdArgs &args,
                       hipStream_t stream);
+// The fp32 kernels of the same three steps (D = 64 or 128).
+hipError_t launch_bwd_f32(int D, bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream);
 
 // Host-side pieces of the key-split path shared by fa_fwd_split and its
 // static-scratch variant (arguments already validated by the caller):

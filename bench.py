@@ -332,18 +332,18 @@ def bench_varlen(name, steps, warmup):
 
 
 def bench_bwd(name, steps, warmup):
-    """fa_bwd on the headline shape, at D = 96 for "bwd_d96*", or B4 H8 N4096
-    at D = 192 / 256 for "bwd_d192*" / "bwd_d256*" (stderr line only).  FLOPs:
-    the five contractions of the backward pass, 10*B*H*N^2*D (2.5x the
-    forward's count, halved for causal); the kernels recompute S and dP once
-    more (seven; eight at D = 256)."""
+    """fa_bwd on the headline shape, at D = 96 for "bwd_d96*", B4 H8 N4096 at
+    D = 192 / 256 for "bwd_d192*" / "bwd_d256*", or the headline shape in fp32
+    for "bwd_f32*" (stderr line only).  FLOPs: the five contractions of the
+    backward pass, 10*B*H*N^2*D (2.5x the forward's count, halved for causal);
+    the kernels recompute S and dP once more (seven; eight at D = 256)."""
     import torch
 
     import attention_fa_fwd_02_amd as fa
     import fa_inputs as fi
     causal = name.endswith("causal")
     D = int(name[5:].split("_")[0]) if name.startswith("bwd_d") else 128
-    B, H, N, dtype = 4, (8 if D > 128 else 16), 4096, "bf16"
+    B, H, N, dtype = 4, (8 if D > 128 else 16), 4096, ("f32" if name.startswith("bwd_f32") else "bf16")
     host, (q, k, v) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0))
     _, (do, _, _) = device_inputs(B, H, N, D, dtype, (1.0, 1.0, 1.0), seed=1004 + 7919)
     scale = 1.0 / math.sqrt(D)
@@ -352,11 +352,12 @@ def bench_bwd(name, steps, warmup):
     wsb = fa.fa_bwd_workspace_bytes(B, H, N, D)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    code = fa.FA_DTYPE_F32 if dtype == "f32" else fa.FA_DTYPE_BF16
 
     def step():
         st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, scale, int(causal),
-                       fa.FA_DTYPE_BF16, ws.data_ptr(), wsb, stream.cuda_stream)
+                       code, ws.data_ptr(), wsb, stream.cuda_stream)
         if st != fa.FA_OK:
             raise fa.FaError(st, "fa_bwd")
 
@@ -372,8 +373,8 @@ def bench_bwd(name, steps, warmup):
     ms = t0.elapsed_time(t1) / steps
     flops = 2.5 * fi.workload_flops(B, H, N, D, causal)
     tf = flops / (ms * 1e-3) / 1e12
-    log("%s: B%d H%d N%d D%d bf16 causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of bf16 peak"
-        % (name, B, H, N, D, causal, ms, tf, 100 * tf / PEAK_TFLOPS["bf16"]))
+    log("%s: B%d H%d N%d D%d %s causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of %s peak"
+        % (name, B, H, N, D, dtype, causal, ms, tf, 100 * tf / PEAK_TFLOPS[dtype], dtype))
 
 
 def bench_fp8(name, steps, warmup):
@@ -475,7 +476,7 @@ def main():
         for name in ("varlen", "varlen_causal"):
             bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
-                     "bwd_d256_causal"):
+                     "bwd_d256_causal", "bwd_f32", "bwd_f32_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("fp8", "fp8_causal", "fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))

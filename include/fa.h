@@ -369,19 +369,20 @@ uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  *   lse               device pointer, fp32 [B, H, N]: the forward logsumexp
  *                     (as fa_fwd writes it) for the same q, k, scale, causal.
  *   dq, dk, dv        device pointers, [B, H, N, D] of element type `dtype`;
- *                     fully overwritten (fp32 accumulation, rounded to nearest
- *                     even once).
+ *                     fully overwritten (fp32 accumulation; 16-bit outputs
+ *                     rounded to nearest even once).
  *   workspace         device pointer, 16-byte aligned, at least
  *                     fa_bwd_workspace_bytes(B, H, N, D) bytes; overwritten.
  *   B, H, N, D, scale, causal, stream  as for fa_fwd.
- *   dtype             FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32:
- *                     FA_ERR_UNSUPPORTED in this build).
+ *   dtype             FA_DTYPE_BF16 or FA_DTYPE_F16 (D = 64, 96, 128, 192,
+ *                     256), or FA_DTYPE_F32 (D = 64 or 128; fp32 matrix
+ *                     instructions, every intermediate in fp32).
  *
  * Errors: FA_ERR_INVALID_ARG for a NULL pointer, B/H/N/D < 1, a non-finite
  * scale, causal not 0/1, an unknown dtype, a tensor or the workspace not
  * 16-byte aligned, lse not 4-byte aligned, workspace_bytes too small, or
  * dq/dk/dv/workspace overlapping each other or any input;
- * FA_ERR_UNSUPPORTED for fp32, D other than 64/96/128/192/256, the size limits of
+ * FA_ERR_UNSUPPORTED for a D outside the dtype's set above, the size limits of
  * fa_fwd, B*H*ceil(N/128) >= 2^23, or a device that is not gfx950;
  * FA_ERR_HIP when a device query or a launch fails.  All checks precede any
  * HIP call; the library allocates nothing.  Every output is written by

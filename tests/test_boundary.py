@@ -399,6 +399,9 @@ def test_bwd_good_arguments_pass():
         for D in (64, 96, 128, 192, 256):
             for c in (0, 1):
                 assert bcheck(dtype=dt, D=D, causal=c) == fa.FA_OK
+    for D in (64, 128):
+        for c in (0, 1):
+            assert bcheck(dtype=0, D=D, causal=c) == fa.FA_OK
     assert bcheck(scale=0.0) == fa.FA_OK and bcheck(scale=-2.0) == fa.FA_OK
 
 
@@ -412,7 +415,8 @@ def test_bwd_invalid_arguments(kw):
     assert bcheck(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=0), dict(D=80), dict(D=160), dict(D=512), dict(N=1 << 30),
+@pytest.mark.parametrize("kw", [dict(dtype=0, D=96), dict(dtype=0, D=256), dict(D=80), dict(D=160), dict(D=512),
+                                dict(N=1 << 30),
                                 dict(B=1 << 14, H=1 << 6, N=128 * 8, wsb=1 << 62)])
 def test_bwd_unsupported(kw):
     assert bcheck(**kw) == fa.FA_ERR_UNSUPPORTED
@@ -421,7 +425,7 @@ def test_bwd_unsupported(kw):
 def test_bwd_reports_invalid_args_before_any_hip_call():
     st = fa.fa_bwd(0, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 128, 0.1, 1, 1, BWS, 12000, 0)
     assert st == fa.FA_ERR_INVALID_ARG
-    st = fa.fa_bwd(BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 128, 0.1, 1, 0, BWS, 12000, 0)
+    st = fa.fa_bwd(BQ, BK, BV, BO, BDO, BL, BDQ, BDK, BDV, 2, 3, 500, 96, 0.1, 1, 0, BWS, 12000, 0)
     assert st == fa.FA_ERR_UNSUPPORTED
 
 

@@ -21,7 +21,13 @@ Tolerance, per element, derived from the arithmetic of the bf16 / fp16 path:
 The bound used is |dX - ref| <= 1e-2 * max(1, A) + E + half an ulp of |ref|
 at every element, E being the propagated forward error above (0 for dV): an
 element formed from small terms answers to 1e-2, as the forward's O does,
-and one formed from large terms gets the same relative room.  A and E are
+and one formed from large terms gets the same relative room.
+
+fp32 inputs (the fp32 kernels: every product and intermediate in fp32, no
+rounding to a narrower type): the per-term error is that of fp32 products
+and sums, about 1e-7 relative, so the bound is 1e-5 * max(1, A) + E, the
+fp32 forward's own 1e-5 with the same relative room, and no output rounding
+term beyond fp32's.  A and E are
 computed in the test from the fp64 P, dP, Delta and O of the definition and
 the device's O (only for the bound; the reference values are the oracle's).
 The largest error, its bound and the tightest margin are printed per case.
@@ -54,7 +60,7 @@ def run_bwd(q, k, v, do, dtype, scale, causal):
     wsb = fa.fa_bwd_workspace_bytes(B, H, N, D)
     ws = torch.full((wsb // 4 + GUARD,), float("nan"), dtype=torch.float32, device="cuda")
     ws[wsb // 4:] = 5.0
-    code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16}[dtype]
+    code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16, "f32": fa.FA_DTYPE_F32}[dtype]
     torch.cuda.synchronize()
     print("fa_bwd B%d H%d N%d D%d %s causal=%d scale=%g" % (B, H, N, D, dtype, causal, scale), flush=True)
     st = fa.fa_bwd(dq_.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), o.data_ptr(), do_.data_ptr(), lse.data_ptr(),
@@ -85,7 +91,8 @@ def check_bwd(B, H, N, D, dtype, causal, seed, scale=None, slices=None):
         for name, got, ref, A, E in zip(("dQ", "dK", "dV"), grads, refs, amag, prop):
             g = _host_widen(got[b, h], dtype)
             err = np.abs(g - ref)
-            tol = 1e-2 * np.maximum(1.0, A) + E + half_ulp(np.abs(ref), dtype)
+            rel = 1e-5 if dtype == "f32" else 1e-2
+            tol = rel * np.maximum(1.0, A) + E + half_ulp(np.abs(ref), dtype)
             e0, t0, m0 = worst.get(name, (-1.0, 0.0, np.inf))
             i = int(np.argmax(err))
             if err.flat[i] > e0:
@@ -123,6 +130,27 @@ def term_magnitudes(q, k, v, do, sc, causal, o_dev):
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ragged(N, D, dtype, causal):
     check_bwd(1, 2, N, D, dtype, causal, seed=700 + N + D)
+
+
+@pytest.mark.parametrize("N", [1, 31, 64, 100, 255, 257, 600])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f32_ragged(N, D, causal):
+    """fp32 inputs (fp32 matrix instructions throughout), ragged N."""
+    check_bwd(1, 2, N, D, "f32", causal, seed=3200 + 17 * N + D)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f32_several_blocks(D, causal):
+    """fp32 over several 128-row query and key blocks with a ragged tail."""
+    check_bwd(2, 2, 700, D, "f32", causal, seed=3900 + D)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.3])
+def test_bwd_f32_scales(scale):
+    """fp32 with a zero, a negative and a large scale."""
+    check_bwd(1, 2, 300, 64, "f32", True, seed=4100, scale=scale)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -174,3 +202,21 @@ def test_bwd_deterministic_and_binding():
     torch.cuda.synchronize()
     for a, b in zip(g1, g3):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bwd_f32_deterministic_and_binding():
+    """fp32: two calls agree bit for bit, and the binding's bwd matches the C ABI call."""
+    import attention_fa_fwd_02_amd as fa
+    torch = _torch()
+    q, k, v = fi.make_qkv(1, 2, 400, 64, "f32", seed=12)
+    do, _, _ = fi.make_qkv(1, 2, 400, 64, "f32", seed=13)
+    g1 = run_bwd(q, k, v, do, "f32", 0.125, True)
+    g2 = run_bwd(q, k, v, do, "f32", 0.125, True)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    dq_, dk_, dv_, do_ = (_to_device(x, "f32") for x in (q, k, v, do))
+    o, lse = fa.fwd(dq_, dk_, dv_, scale=0.125, causal=True)
+    g3 = fa.bwd(dq_, dk_, dv_, o, lse, do_, scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g3):
+        assert torch.equal(a, b)
