@@ -136,6 +136,44 @@ struct TilePair {
     }
 };
 
+// One R-row tile X in the same layout, filled the same way (blocks [0, NX)
+// hold X, the rest are spare).
+template <int W, int R, int D, int P>
+struct Tile1 {
+    static constexpr int NX = R * P / 1024;
+    static_assert(NX * 1024 == R * P, "a tile is a whole number of 1 KB blocks");
+    static constexpr int LPW = (NX + W - 1) / W;
+    static constexpr int BYTES = 1024 * W * LPW;
+    static_assert(R * D * 2 <= 65536, "tile offsets fit in 16 bits");
+    uint32_t voff2[(LPW + 1) / 2];
+
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < (LPW + 1) / 2; ++j)
+            voff2[j] = 0u;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int blk = wave + W * j;
+            const int pos = 1024 * blk + 16 * lane;
+            const int row = pos / P, o = pos % P - row_shift(row);
+            const int chunk = o / 16;
+            const bool data = blk < NX && o >= 0 && chunk < D / 8;
+            const uint32_t off = data ? (uint32_t)(row * D + 8 * chunk) * 2u : 0u;
+            voff2[j / 2] |= off << (16 * (j % 2));
+        }
+    }
+    // rows row0 .. row0 + R - 1 of X; rows at or past n_rows read as zeros
+    __device__ __forceinline__ void issue(const uint16_t *X, int row0, int n_rows, lds_char *st, int wave) const {
+        const uint32_t bytes =
+            __builtin_amdgcn_readfirstlane((uint32_t)(min(max(n_rows - row0, 0), R) * D * 2));
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const uint32_t off = (j % 2) ? (voff2[j / 2] >> 16) : (voff2[j / 2] & 0xFFFFu);
+            load_lds_16(X + (int64_t)row0 * D, bytes, off, st + 1024 * (wave + W * j));
+        }
+    }
+};
+
 // ----------------------------------------------------------------------------
 // Delta_i = dO_i . O_i (fp32), one row per D/8 lanes
 // ----------------------------------------------------------------------------
@@ -676,6 +714,269 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// ----------------------------------------------------------------------------
+// dK, dV at D <= 128: 128 keys per workgroup, 8 waves (two per SIMD)
+// ----------------------------------------------------------------------------
+// Waves w and w + 4 share a SIMD and the same 32 keys (32 (w % 4) of the
+// block); wave w takes the first 32 queries of every 64-query tile, wave
+// w + 4 the last 32, each accumulating its own partial dV^T and dK^T.  With
+// two waves per SIMD, one wave's LDS reads (the transposing reads of the
+// dV / dK products above all) overlap the other's MFMAs.  To fit two waves
+// in a SIMD's registers the block's V rows stay in LDS (read as B operands
+// per MFMA); the K rows stay in registers.  At the end the waves of the
+// second query half hand their partial sums to the first through LDS.
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void fa_bwd_dkdv8_kernel(BwdArgs a) {
+    constexpr int W = 8, BK = 128, TQ = 64, DC = D / 16, OB = D / 32;
+    constexpr int P = 2 * D + 32; // row pitch of every tile (rows with bit 3 set shifted by 16)
+    constexpr int OP = 2 * D + 16; // dK / dV staging pitch
+    using VT = Tile1<W, BK, D, P>;      // the block's V rows, loaded once
+    using Tiles = TilePair<W, TQ, D, P>; // per stage: the Q and dO tiles
+    constexpr int STAT = Tiles::BYTES;
+    // then one 256-byte slot per wave for the lse / Delta loads: slot 0 lse,
+    // slot 1 Delta (the other waves load lse into their own slots)
+    constexpr int STAGE = STAT + 256 * W;
+    static_assert(VT::BYTES % 16 == 0 && STAGE % 16 == 0, "16-byte aligned areas");
+    // one array: the V area, then the two stages
+    __shared__ __attribute__((aligned(16))) char smem_raw[VT::BYTES + 2 * STAGE];
+    lds_char *const vsh = (lds_char *)smem_raw;
+    lds_char *const stage0 = vsh + VT::BYTES;
+    lds_char *const stage1 = stage0 + STAGE;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kw = wave & 3, qh = wave >> 2; // key group, query half
+    const int r = lane & 31;
+    const int g = lane >> 5;
+    const int N = a.N;
+    const int n_kblk = (N + BK - 1) / BK;
+    const Blk wk = map_bwd(blockIdx.x, gridDim.x, n_kblk, false);
+    const int64_t slice = (int64_t)wk.bh * N * D;
+    const uint16_t *__restrict__ Q = (const uint16_t *)a.q + slice;
+    const uint16_t *__restrict__ K = (const uint16_t *)a.k + slice;
+    const uint16_t *__restrict__ V = (const uint16_t *)a.v + slice;
+    const uint16_t *__restrict__ dO = (const uint16_t *)a.dout + slice;
+    const float *__restrict__ LSE = a.lse + (int64_t)wk.bh * N;
+    const float *__restrict__ DL = a.delta + (int64_t)wk.bh * N;
+    uint16_t *__restrict__ dK = (uint16_t *)a.dk + slice;
+    uint16_t *__restrict__ dV = (uint16_t *)a.dv + slice;
+
+    const int k0 = wk.blk * BK;
+    const int k0w = k0 + 32 * kw;
+    const int kj = k0w + r; // this lane's key
+    const int t_begin = CAUSAL ? k0 / TQ : 0;
+    const int n_tiles = (N + TQ - 1) / TQ;
+
+    {
+        VT vt;
+        vt.init(wave, lane);
+        vt.issue(V, k0, N, vsh, wave);
+    }
+    Tiles tiles;
+    tiles.init(wave, lane);
+    // lse / Delta loads: lane l fills float l of the slot with query
+    // 32 (l/32) + 2 (l%16) + (l/16)%2 of the tile, so a lane half g finds the
+    // queries of its accumulator entries (2i + g) as 16 consecutive floats
+    const uint32_t stat_off = 4u * (uint32_t)(32 * (lane >> 5) + 2 * (lane & 15) + ((lane >> 4) & 1));
+    // load j (0 .. NLD - 1) of tile t: the wave's Q / dO blocks, then its stat load
+    constexpr int NLD = Tiles::LPW + 1;
+    auto issue_one = [&](int t, lds_char *st, int j) __attribute__((always_inline)) {
+        const int i0 = t * TQ;
+        if (j < Tiles::LPW) {
+            tiles.issue_one(Q, dO, i0, N, st, wave, j);
+        } else {
+            const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(min(max(N - i0, 0), TQ) * 4));
+            load_lds_4((wave == 1 ? DL : LSE) + i0, sb, stat_off, st + STAT + 256 * wave);
+        }
+    };
+    auto issue = [&](int t, lds_char *st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+            issue_one(t, st, j);
+    };
+    // A operand rows of this wave's query half, B operand rows of its keys
+    const int q_lane = (32 * qh + perm_row(r)) * P + row_shift(perm_row(r)) + 16 * g;
+    const int v_lane = (32 * kw + r) * P + row_shift(r) + 16 * g;
+    const int t_lane = (32 * qh) * P + tr_lane(lane, P);
+    const float c2 = a.c2;
+    // B operand of S = Q K^T: lane (r, g) holds k_kj[16c + 8g ..]
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    u32x4 kf[DC];
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc)
+        kf[cc] = kj < N ? *(const u32x4 *)(K + (int64_t)kj * D + 16 * cc + 8 * g) : zero4;
+
+    f32x16 dva[OB], dka[OB];
+#pragma unroll
+    for (int b = 0; b < OB; ++b) {
+        dva[b] = f32x16{};
+        dka[b] = f32x16{};
+    }
+
+    // the next tile's loads go out first (past the last tile they read zeros
+    // into the idle stage)
+    auto tile = [&](int t, const lds_char *cur, lds_char *next) {
+        const int i0 = t * TQ;
+        issue(t + 1, next);
+        const int iq = i0 + 32 * qh; // first query of this wave's half
+        const bool active = (k0w < N) && (iq < N) && (!CAUSAL || iq + 31 >= k0w);
+        if (active) {
+            const lds_char *qs = cur + q_lane;
+            const lds_char *ds = cur + Tiles::NX * 1024 + q_lane;
+            const lds_char *vs = vsh + v_lane;
+            // S = Q K^T and dP = dO V^T for the wave's 32 queries
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                s = E::mfma(lds_u32x4(qs + 32 * cc), kf[cc], s);
+                dp = E::mfma(lds_u32x4(ds + 32 * cc), lds_u32x4(vs + 32 * cc), dp);
+            }
+            // three reads ahead, then per MFMA its reads (one for S, two for dP)
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+            for (int n = 0; n < 2 * DC - 2; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (n % 2 == 1)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // P = exp2(c2 s - log2(e) lse_i), dS = P (dP - Delta_i); causal: a
+            // query before the key gets P = 0.  Entry i of lane (r, g) is query
+            // iq + 2 i + g.
+            const bool diag = CAUSAL && iq < k0w + 31;
+            const int lim = kj - iq - g;
+            const lds_char *stat = cur + STAT + 64 * g + 128 * qh;
+            uint32_t pp[8], pd[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 16 * m);
+                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(stat + 256 + 16 * m);
+                float pv[4], sv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = 4 * m + u;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l4[u] * kLog2e));
+                    if (diag)
+                        p = (2 * i >= lim) ? p : 0.f;
+                    pv[u] = p;
+                    sv[u] = p * (dp[i] - d4[u]);
+                }
+                pp[2 * m] = E::pack(pv[0], pv[1]);
+                pp[2 * m + 1] = E::pack(pv[2], pv[3]);
+                pd[2 * m] = E::pack(sv[0], sv[1]);
+                pd[2 * m + 1] = E::pack(sv[2], sv[3]);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries
+            const lds_char *qt = cur + t_lane;
+            const lds_char *dt = cur + Tiles::NX * 1024 + t_lane;
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int off = 16 * mm * P + 64 * b;
+                    const u32x4 pv = {pp[4 * mm], pp[4 * mm + 1], pp[4 * mm + 2], pp[4 * mm + 3]};
+                    const u32x4 sv = {pd[4 * mm], pd[4 * mm + 1], pd[4 * mm + 2], pd[4 * mm + 3]};
+                    dva[b] = E::mfma(tr_read(dt + off, P), pv, dva[b]);
+                    dka[b] = E::mfma(tr_read(qt + off, P), sv, dka[b]);
+                }
+            // the transposing reads of four MFMAs ahead, then two after each MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int n = 0; n < 4 * OB - 4; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        wait_vmcnt<0>();
+        tile_barrier();
+    };
+
+    issue(t_begin, stage0);
+    wait_vmcnt<0>();
+    tile_barrier();
+    int t = t_begin;
+    for (; t + 2 <= n_tiles; t += 2) {
+        tile(t, stage0, stage1);
+        tile(t + 1, stage1, stage0);
+    }
+    if (t < n_tiles)
+        tile(t, stage0, stage1);
+
+    // the second query half's partial sums, through LDS (the whole array is
+    // free after the loop's last barrier), dV then dK: wave w + 4 writes its
+    // accumulators in lane order, wave w adds them to its own
+    constexpr int PART = OB * 16 * 64 * 4; // one wave's dV (or dK) partial (bytes)
+    static_assert(4 * PART <= VT::BYTES + 2 * STAGE, "the partials fit the block's LDS");
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    lds_f32x4 *const part = (lds_f32x4 *)(vsh + kw * PART + 16 * lane);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        f32x16(&acc)[OB] = pass == 0 ? dva : dka;
+        if (qh == 1) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 x = {acc[b][4 * q4], acc[b][4 * q4 + 1], acc[b][4 * q4 + 2], acc[b][4 * q4 + 3]};
+                    part[64 * (4 * b + q4)] = x;
+                }
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 x = part[64 * (4 * b + q4)];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc[b][4 * q4 + u] += x[u];
+                }
+        }
+        __syncthreads();
+    }
+
+    // epilogue (waves of the first query half): dV and dK = scale * acc; entry
+    // i of lane (r, g) in block b is feature 32 b + 8 (i/4) + 4 g + i%4 of key
+    // kj; staged through LDS per wave, 16-byte stores
+    static_assert(4 * 32 * OP <= VT::BYTES, "four waves' rows fit the V area");
+    lds_char *ow = vsh + kw * 32 * OP;
+    const float sc = a.scale;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        uint16_t *__restrict__ OUT = pass == 0 ? dV : dK;
+        if (qh == 0 && k0w < N) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x16 &x = pass == 0 ? dva[b] : dka[b];
+                    const float f = pass == 0 ? 1.f : sc;
+                    const u32x2 w = {E::pack(x[4 * a4] * f, x[4 * a4 + 1] * f),
+                                     E::pack(x[4 * a4 + 2] * f, x[4 * a4 + 3] * f)};
+                    *(__attribute__((address_space(3))) u32x2 *)(ow + r * OP + (32 * b + 8 * a4 + 4 * g) * 2) = w;
+                }
+        }
+        __syncthreads();
+        if (qh == 0 && k0w < N) {
+#pragma unroll
+            for (int j = 0; j < 32 * (D / 8) / 64; ++j) {
+                const int ch = 64 * j + lane;
+                const int row = ch / (D / 8), col = ch % (D / 8);
+                const int key = k0w + row;
+                const u32x4 val = lds_u32x4(ow + row * OP + col * 16);
+                if (key < N)
+                    *(u32x4 *)(OUT + (int64_t)key * D + col * 8) = val;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <typename E, int D>
 hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
     const int64_t rows = BH * args.N;
@@ -695,6 +996,8 @@ hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_
                                args);
             hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, C, kDkOnly>), dim3((unsigned)n_k), dim3(256), 0, stream,
                                args);
+        } else if constexpr (D <= 128) {
+            hipLaunchKernelGGL((fa_bwd_dkdv8_kernel<E, D, C>), dim3((unsigned)n_k), dim3(512), 0, stream, args);
         } else {
             hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, C, kDkDv>), dim3((unsigned)n_k), dim3(256), 0, stream,
                                args);
