@@ -21,7 +21,9 @@
 //                        two 32-key halves staggered as in the dK/dV kernel;
 //   fa_bwd_dkdv_kernel   one workgroup per 128 keys (4 waves x 32 keys), looping
 //                        over 64-query tiles of Q and dO: S = Q K^T, dP = dO V^T,
-//                        dS, then dV^T += dO^T P and dK^T += Q^T dS.  At D = 256
+//                        dS, then dV^T += dO^T P and dK^T += Q^T dS (at D <= 128
+//                        fa_bwd_dkdv8_kernel does the same with 8 waves, two per
+//                        SIMD, each taking half of every query tile).  At D = 256
 //                        the two accumulators, K and V do not fit one wave's
 //                        registers together: one launch accumulates dV (S and
 //                        dV^T only), a second dK (S, dP and dK^T).
