@@ -8,9 +8,12 @@ Throughput counts 4*B*H*N^2*D FLOPs per step (half for causal).
 The default run also times every other configuration of the five synthetic
 workloads (tiny fp32; small bf16 both modes and fp32; the headline shape
 causal; wide D = 64; long-context causal) with the same step and warm-up
-counts and reports them in the JSON line's "workloads" object.  Warm-up runs
-at least --warmup steps and at least --warm-seconds of GPU work, so that the
-clocks have settled before the timed steps.
+counts and reports them in the JSON line's "workloads" object, and the next
+rows of the path on their own workloads (the backward pass, the key split,
+packed sequences and FP8 inputs, both modes, a fifth of the steps) in its
+"next_rows" object.  Warm-up runs at least --warmup steps and at least
+--warm-seconds of GPU work, so that the clocks have settled before the timed
+steps.
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
@@ -285,8 +288,33 @@ def bench_one(name, steps, warmup, copy_calibration=False, flush=False, warm_sec
     return res, (host, (o, lse), B, H, N, D, dtype, causal)
 
 
-def bench_varlen(name, steps, warmup):
-    """The packed length-mix workload through fa_fwd_varlen (stderr line only)."""
+def time_steps(step, steps, warmup, warm_seconds):
+    """Warm up (at least `warmup` calls and `warm_seconds` of wall time), then
+    time `steps` back-to-back calls between two events on the current stream;
+    returns ms per call."""
+    import torch
+    stream = torch.cuda.current_stream()
+    warm_up(step, warmup, warm_seconds)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def next_row(name, config, ms, flops, peak_dtype):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"name": name, "config": config, "ms_per_step": round(ms, 5), "tflops": round(tf, 3),
+            "peak": PEAK_TFLOPS[peak_dtype], "peak_dtype": peak_dtype,
+            "frac": round(tf / PEAK_TFLOPS[peak_dtype], 4)}
+
+
+def bench_varlen(name, steps, warmup, warm_seconds=0.0):
+    """The packed length-mix workload through fa_fwd_varlen; logs a stderr
+    line and returns the result record."""
     import numpy as np
     import torch
 
@@ -315,28 +343,23 @@ def bench_varlen(name, steps, warmup):
         if st != fa.FA_OK:
             raise fa.FaError(st, "fa_fwd_varlen")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = time_steps(step, steps, warmup, warm_seconds)
     flops = fi.varlen_flops(lens, lens, H, D, causal)
     log("%s: %d packed sequences (%d..%d rows, %d total) H%d D%d bf16 causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of bf16 peak"
         % (name, len(lens), int(lens.min()), max_len, total, H, D, causal, ms, flops / (ms * 1e-3) / 1e12,
            100 * flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"]))
+    return next_row(name, "fa_fwd_varlen: %d packed sequences of %d..%d rows (%d total), H%d D%d bf16 %s"
+                    % (len(lens), int(lens.min()), max_len, total, H, D, "causal" if causal else "non-causal"),
+                    ms, flops, "bf16")
 
 
-def bench_bwd(name, steps, warmup):
+def bench_bwd(name, steps, warmup, warm_seconds=0.0):
     """fa_bwd on the headline shape, at D = 96 for "bwd_d96*", B4 H8 N4096 at
     D = 192 / 256 for "bwd_d192*" / "bwd_d256*", or the headline shape in fp32
     for "bwd_f32*" (stderr line only).  FLOPs: the five contractions of the
     backward pass, 10*B*H*N^2*D (2.5x the forward's count, halved for causal);
-    the kernels recompute S and dP once more (seven; eight at D = 256)."""
+    the kernels recompute S and dP once more (seven; eight at D = 256).
+    Returns the result record."""
     import torch
 
     import attention_fa_fwd_02_amd as fa
@@ -361,23 +384,16 @@ def bench_bwd(name, steps, warmup):
         if st != fa.FA_OK:
             raise fa.FaError(st, "fa_bwd")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = time_steps(step, steps, warmup, warm_seconds)
     flops = 2.5 * fi.workload_flops(B, H, N, D, causal)
     tf = flops / (ms * 1e-3) / 1e12
     log("%s: B%d H%d N%d D%d %s causal=%d  step %.4f ms  %.1f TFLOP/s  %.1f%% of %s peak"
         % (name, B, H, N, D, dtype, causal, ms, tf, 100 * tf / PEAK_TFLOPS[dtype], dtype))
+    return next_row(name, "fa_bwd: B%d H%d N%d D%d %s %s (10 B H N^2 D flops, halved for causal)"
+                    % (B, H, N, D, dtype, "causal" if causal else "non-causal"), ms, flops, dtype)
 
 
-def bench_fp8(name, steps, warmup):
+def bench_fp8(name, steps, warmup, warm_seconds=0.0):
     """fa_fwd_fp8 on the headline shape (B4 H16 N4096 D128, E4M3 inputs, bf16 O),
     or B4 H8 N4096 at head dim 96 / 192 / 256 (stderr line only).  FLOPs as for
     the 16-bit path; peak: dense FP8 MFMA."""
@@ -405,19 +421,13 @@ def bench_fp8(name, steps, warmup):
         if st != fa.FA_OK:
             raise fa.FaError(st, "fa_fwd_fp8")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    tf = fi.workload_flops(B, H, N, D, causal) / (ms * 1e-3) / 1e12
+    ms = time_steps(step, steps, warmup, warm_seconds)
+    flops = fi.workload_flops(B, H, N, D, causal)
+    tf = flops / (ms * 1e-3) / 1e12
     log("%s: B%d H%d N%d D%d e4m3 causal=%d  step %.4f ms (V transpose included)  %.1f TFLOP/s  %.1f%% of fp8 peak"
         % (name, B, H, N, D, causal, ms, tf, 100 * tf / PEAK_TFLOPS["e4m3"]))
+    return next_row(name, "fa_fwd_fp8: B%d H%d N%d D%d e4m3 %s (V transpose included)"
+                    % (B, H, N, D, "causal" if causal else "non-causal"), ms, flops, "e4m3")
 
 
 def main():
@@ -467,18 +477,33 @@ def main():
                 "frac": round(r["achieved"] / r["peak"], 4), "kernel": r["kernel"],
                 "kernel_avg_ms": round(r["kernel_ms"], 5), "kernel_median_ms": round(r["kernel_median_ms"], 5),
                 "kernel_min_ms": round(r["kernel_min_ms"], 5)}
+    next_rows = None
+    if not args.no_workloads:
+        # the next rows of the path on their own workloads (backward, key split,
+        # packed sequences, FP8), both modes, fewer steps
+        ns, nw = max(10, args.steps // 5), max(10, args.warmup // 5)
+        next_rows = {}
+        for name in ("bwd", "bwd_causal"):
+            next_rows[name] = bench_bwd(name, ns, nw, warm_seconds=0.3)
+        for name in SPLIT_WORKLOADS:
+            r, _ = bench_one(name, ns, nw, warm_seconds=0.3)
+            next_rows[name] = next_row(name, "fa_fwd_split: B%d H%d N%d D%d %s %s, %s" % (
+                r["B"], r["H"], r["N"], r["D"], r["dtype"], "causal" if r["causal"] else "non-causal", r["kernel"]),
+                r["ms_per_step"], r["flops"], r["dtype"])
+        for name in ("varlen", "varlen_causal"):
+            next_rows[name] = bench_varlen(name, ns, nw, warm_seconds=0.3)
+        for name in ("fp8", "fp8_causal"):
+            next_rows[name] = bench_fp8(name, ns, nw, warm_seconds=0.3)
     if args.all:
         # every GPU timing comes before the CPU-oracle leg, whose minutes of host
         # work would otherwise leave the GPU idle (and down-clocked) right before
-        for name in list(WORKLOADS) + list(SPLIT_WORKLOADS):
+        for name in WORKLOADS:
             if name != args.workload:
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), warm_seconds=0.5)
-        for name in ("varlen", "varlen_causal"):
-            bench_varlen(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("bwd", "bwd_causal", "bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
+        for name in ("bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
                      "bwd_d256_causal", "bwd_f32", "bwd_f32_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("fp8", "fp8_causal", "fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
+        for name in ("fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     if args.flush:
         for name in ("headline", "headline_causal"):
@@ -516,6 +541,8 @@ def main():
     }
     if workloads is not None:
         out["workloads"] = workloads
+    if next_rows is not None:
+        out["next_rows"] = next_rows
     print(json.dumps(out), flush=True)
 
 
