@@ -10,15 +10,16 @@
 //   dS = P * (dP - Delta),   dQ = scale * dS K,   dK = scale * dS^T Q.
 // Delta_i equals dO_i . O_i because O_i = sum_j P_ij v_j.
 //
-// Three kernels on one stream:
-//   fa_bwd_delta_kernel  Delta = rowsum(dO * O) in fp32 (memory-bound);
+// Two kernels on one stream:
 //   fa_bwd_dq_kernel     one workgroup per 256 query rows (8 waves x 32 rows;
 //                        4 waves and 128 rows at D > 128, where a wave's
 //                        operands and accumulators need a SIMD's whole
 //                        register file), looping over 64-key tiles of K and
-//                        V: S^T = K Q^T,
-//                        dP^T = V dO^T, dS, then dQ^T += K^T dS^T, the tile's
-//                        two 32-key halves staggered as in the dK/dV kernel;
+//                        V: S^T = K Q^T, dP^T = V dO^T, dS, then dQ^T += K^T
+//                        dS^T, the tile's two 32-key halves staggered as in the
+//                        dK/dV kernel; before its loop it forms Delta_i =
+//                        dO_i . O_i of its rows (fp32) and writes it to the
+//                        workspace for the dK/dV kernel;
 //   fa_bwd_dkdv_kernel   one workgroup per 128 keys (4 waves x 32 keys), looping
 //                        over 64-query tiles of Q and dO: S = Q K^T, dP = dO V^T,
 //                        dS, then dV^T += dO^T P and dK^T += Q^T dS (at D <= 128
@@ -177,45 +178,6 @@ struct Tile1 {
 };
 
 // ----------------------------------------------------------------------------
-// Delta_i = dO_i . O_i (fp32), one row per D/8 lanes
-// ----------------------------------------------------------------------------
-// Lanes per row of the Delta kernel: the largest power of two dividing the
-// row's D / 8 sixteen-byte chunks (the row sum is a shuffle over them).
-constexpr int delta_lanes(int D) { return (D / 8) & -(D / 8); }
-
-template <typename E, int D>
-__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t *__restrict__ O,
-                                                           const uint16_t *__restrict__ dO,
-                                                           float *__restrict__ delta, int64_t rows) {
-    constexpr int TPR = delta_lanes(D); // lanes per row (D 64..256: 8, 4, 16, 8, 32)
-    constexpr int CPL = D / 8 / TPR;    // 16-byte chunks per lane (1, 3, 1, 3, 1)
-    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = item / TPR;
-    const int c = (int)(item % TPR);
-    float acc = 0.f;
-    if (row < rows) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const u32x4 ov = *(const u32x4 *)(O + row * D + 8 * (c + TPR * j));
-            const u32x4 dv = *(const u32x4 *)(dO + row * D + 8 * (c + TPR * j));
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const f32x2 a = E::unpack(ov[w]);
-                const f32x2 b = E::unpack(dv[w]);
-                acc = __builtin_fmaf(a[0], b[0], acc);
-                acc = __builtin_fmaf(a[1], b[1], acc);
-            }
-        }
-    }
-    // sum over the TPR lanes of the row (aligned groups of a wave)
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1)
-        acc += __shfl_xor(acc, m, 64);
-    if (row < rows && c == 0)
-        delta[row] = acc;
-}
-
-// ----------------------------------------------------------------------------
 // dQ: 32 query rows per wave, 64-key tiles
 // ----------------------------------------------------------------------------
 // Waves per dQ workgroup: 8 (two per SIMD) while a wave's Q and dO operands
@@ -269,7 +231,28 @@ __global__ __launch_bounds__(64 * dq_waves(D)) void fa_bwd_dq_kernel(BwdArgs a) 
         df[cc] = qi < N ? *(const u32x4 *)(dO + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
     }
     const float nl = qi < N ? -a.lse[(int64_t)wk.bh * N + qi] * kLog2e : 0.f;
-    const float dl = qi < N ? a.delta[(int64_t)wk.bh * N + qi] : 0.f;
+    // Delta_i = dO_i . O_i in fp32: each lane of the pair takes the features
+    // its dO operand holds, the pair adds the halves; lane g = 0 writes Delta
+    // for the dK/dV kernel, which runs after this one on the stream
+    float dl;
+    {
+        const uint16_t *__restrict__ Ob = (const uint16_t *)a.o + slice;
+        float part = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) {
+            const u32x4 ov = qi < N ? *(const u32x4 *)(Ob + (int64_t)qi * D + 16 * cc + 8 * g) : zero4;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2 x = E::unpack(ov[w]);
+                const f32x2 y = E::unpack(df[cc][w]);
+                part = __builtin_fmaf(x[0], y[0], part);
+                part = __builtin_fmaf(x[1], y[1], part);
+            }
+        }
+        dl = pair_sum(part);
+        if (g == 0 && qi < N)
+            a.delta[(int64_t)wk.bh * N + qi] = dl;
+    }
     const float c2 = a.c2;
 
     f32x16 acc[OB];
@@ -981,13 +964,6 @@ __global__ __launch_bounds__(512) void fa_bwd_dkdv8_kernel(BwdArgs a) {
 
 template <typename E, int D>
 hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
-    const int64_t rows = BH * args.N;
-    const int64_t items = rows * delta_lanes(D);
-    hipLaunchKernelGGL((fa_bwd_delta_kernel<E, D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream,
-                       (const uint16_t *)args.o, (const uint16_t *)args.dout, args.delta, rows);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
     constexpr int WQ = dq_waves(D);
     const int64_t n_q = BH * ((args.N + 32 * WQ - 1) / (32 * WQ));
     const int64_t n_k = BH * ((args.N + 127) / 128);

@@ -360,8 +360,9 @@ fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const v
 uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
 
 /*
- * fa_bwd -- enqueue the backward pass on `stream` (three kernels: Delta, dQ,
- * dK/dV; at D = 256 dV and dK are two launches of the last).
+ * fa_bwd -- enqueue the backward pass on `stream` (16-bit: a dQ kernel that
+ * also forms Delta, then a dK/dV kernel, two launches of it at D = 256;
+ * fp32: Delta, dQ and dK/dV kernels).
  *
  *   q, k, v, o, dout  device pointers, [B, H, N, D] of element type `dtype`,
  *                     read-only: the forward inputs, its output O and the
