@@ -21,6 +21,7 @@ SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
            os.path.join(CSRC, "fa_bwd_f32.hip"),
            os.path.join(CSRC, "fa_fp8.hip"), os.path.join(CSRC, "fa_static.hip")]
 HEADERS = [os.path.join(CSRC, "fa_internal.h"), os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_fwd_common.h"),
+           os.path.join(CSRC, "fa_bwd_common.h"),
            os.path.join(ROOT, "include", "fa.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

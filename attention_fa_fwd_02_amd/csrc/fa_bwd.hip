@@ -42,7 +42,7 @@
 // products, with dO^T and Q^T read transposed from LDS.  Tiles reach LDS by
 // direct-to-LDS buffer loads (rows past the end read as zeros), double
 // buffered with one barrier per tile.
-#include "fa_device.h"
+#include "fa_bwd_common.h"
 #include "fa_internal.h"
 
 #include <type_traits>

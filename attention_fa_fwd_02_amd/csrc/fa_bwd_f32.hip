@@ -34,7 +34,7 @@
 // conflict on those reads.  Every read is an immediate offset from one
 // per-lane base.  The tiles are filled by 4-byte direct-to-LDS loads, each
 // lane fetching the element its LDS slot holds.
-#include "fa_device.h"
+#include "fa_bwd_common.h"
 #include "fa_internal.h"
 
 namespace fa {

@@ -22,7 +22,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.44269504088896340736f;
 // Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data format,
 // no swizzle, so loads address plain bytes and are range-checked against the
 // descriptor's record count (out-of-range loads return zeros).
@@ -59,13 +58,6 @@ __device__ __forceinline__ void load_lds_16(const void *base, uint32_t bytes, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
 }
 
-// Direct global -> LDS load of 4 bytes per lane (lane l writes lds + 4 l).
-__device__ __forceinline__ void load_lds_4(const void *base, uint32_t bytes, uint32_t voff, lds_char *lds) {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
-}
-
 // Max / sum over the lane pair (l, l^32) that shares one query row.
 __device__ __forceinline__ float pair_max(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -76,26 +68,6 @@ __device__ __forceinline__ float pair_sum(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return __builtin_bit_cast(float, (uint32_t)s[0]) + __builtin_bit_cast(float, (uint32_t)s[1]);
-}
-
-// Backward kernels: workgroups go round-robin over the 8 XCDs (id % 8); with a grid that is a
-// multiple of 8, XCD x takes the contiguous logical range [x n/8, (x+1) n/8),
-// so the blocks of one (batch, head) slice share an L2.  `reverse` hands the
-// blocks of a slice out last index first.
-struct Blk {
-    int bh;
-    int blk;
-};
-__device__ __forceinline__ Blk map_bwd(int wg, int nwg, int n_blk, bool reverse) {
-    int L = wg;
-    if ((nwg & 7) == 0)
-        L = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    Blk b;
-    b.bh = L / n_blk;
-    b.blk = L - b.bh * n_blk;
-    if (reverse)
-        b.blk = n_blk - 1 - b.blk;
-    return b;
 }
 
 struct Work {
