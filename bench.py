@@ -497,6 +497,16 @@ def main():
     if args.all:
         # every GPU timing comes before the CPU-oracle leg, whose minutes of host
         # work would otherwise leave the GPU idle (and down-clocked) right before
+        if next_rows is None:  # --no-workloads: the next rows on stderr only
+            ns, nw = max(10, args.steps // 5), max(10, args.warmup // 5)
+            for name in ("bwd", "bwd_causal"):
+                bench_bwd(name, ns, nw)
+            for name in SPLIT_WORKLOADS:
+                bench_one(name, ns, nw, warm_seconds=0.5)
+            for name in ("varlen", "varlen_causal"):
+                bench_varlen(name, ns, nw)
+            for name in ("fp8", "fp8_causal"):
+                bench_fp8(name, ns, nw)
         for name in WORKLOADS:
             if name != args.workload:
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), warm_seconds=0.5)
