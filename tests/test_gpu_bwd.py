@@ -167,6 +167,21 @@ def test_bwd_wide_heads_several_blocks(D, causal):
     check_bwd(1, 2, 700, D, "bf16", causal, seed=1920 + D)
 
 
+@pytest.mark.parametrize("D,causal", [(192, False), (256, False), (256, True)])
+def test_bwd_wide_heads_full_size_slice(D, causal):
+    """B4 H8 N4096 at D = 192 and 256, the shapes and launches bench.py times:
+    one seeded (b, h) slice, every row."""
+    slices = fi.sample_slices(4, 8, 1, seed=41 + D + int(causal))
+    check_bwd(4, 8, 4096, D, "bf16", causal, seed=1004, slices=slices)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f32_headline_slice(causal):
+    """fp32 at the headline shape (B4 H16 N4096 D128), one seeded slice, every row."""
+    slices = fi.sample_slices(4, 16, 1, seed=43 + int(causal))
+    check_bwd(4, 16, 4096, 128, "f32", causal, seed=1004, slices=slices)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_workload(causal):
     w = fi.WORKLOADS["small_bf16"]
