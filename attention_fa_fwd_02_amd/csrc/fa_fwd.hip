@@ -161,6 +161,8 @@ struct MfmaCfg {
     static_assert(LDS <= 160 * 1024, "fits the 160 KB LDS of a CU");
     // two wave groups per SIMD and 128-key tiles: the ping-pong schedule
     static constexpr bool PINGPONG = WAVES == 8 && BC == 128;
+    // 64-key tiles (D = 192): the ping-pong schedule for whole slices only
+    static constexpr bool PP_DENSE = WAVES == 8;
 };
 
 // Position of the i-th of NL tile loads among NM MFMAs of one phase: after
@@ -564,8 +566,9 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_mfma_kernel(FwdArg
 
 // ----------------------------------------------------------------------------
 // bf16 / fp16 MFMA kernel, ping-pong schedule ([B, H, N, D] slices, whole or
-// split over keys, and packed sequences without the causal mask; head dims
-// with 128-key tiles)
+// split over keys, and packed sequences without the causal mask, at head dims
+// with 128-key tiles; whole slices without the causal mask at D = 192, with
+// 64-key tiles)
 // ----------------------------------------------------------------------------
 // Same tiles, operand layouts, masking and online softmax as
 // fa_fwd_mfma_kernel; only the order of work differs.  (Causal packed
@@ -599,7 +602,7 @@ template <typename E, int D, bool CAUSAL, int MODE, int KG>
 __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs a) {
     constexpr bool SPLIT = MODE == kSplit, VARLEN = MODE == kVarlen;
     using Cfg = MfmaCfg<D>;
-    static_assert(Cfg::PINGPONG, "two wave groups of four, 128-key tiles");
+    static_assert(Cfg::PINGPONG || (Cfg::PP_DENSE && MODE == kDense && KG == 1), "two wave groups of four");
     static_assert(KG == 1 || ((KG == 2 || KG == 4) && MODE == kDense), "key groups of whole slices");
     constexpr int W = Cfg::WAVES, BC = Cfg::BC;
     constexpr int BCS = BC / KG;         // keys of a wave's share of a tile
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(MfmaCfg<D>::THREADS) void fa_fwd_pp_kernel(FwdArgs 
     //    leaves slack.  (At D = 128 the spread loader's 18 offsets per wave
     //    would also make the causal instances spill.)
     constexpr bool SPREAD = !(KG == 1 && (D == 128 || (D == 96 && CAUSAL)));
-    constexpr int IW = SPREAD ? 4 : W, LPI = (NK + NV + IW - 1) / IW;
+    constexpr int IW = SPREAD ? 4 : W, LPI = W * LPW / IW;
     static_assert(IW * LPI == W * LPW, "same stage layout");
     const int iwave = SPREAD ? (wave & 3) : wave;
     uint32_t voff2[(LPI + 1) / 2];
@@ -1381,6 +1384,10 @@ hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_
         }
         return launch_pp<E, D, MODE, 1>(causal, nwg, args, stream);
     } else {
+        if constexpr (MODE == kDense && MfmaCfg<D>::PP_DENSE) {
+            if (kg == 1 && !causal) // (the causal instance spills at 64-key tiles)
+                return launch<fa_fwd_pp_kernel<E, D, false, MODE, 1>, T>(nwg, 0, args, stream);
+        }
         if (causal)
             return launch<fa_fwd_mfma_kernel<E, D, true, MODE>, T>(nwg, 0, args, stream);
         return launch<fa_fwd_mfma_kernel<E, D, false, MODE>, T>(nwg, 0, args, stream);
@@ -1463,7 +1470,7 @@ const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg)
                             if (t == 0)
                                 snprintf(out, 96, "fa_fwd_f32_kernel<%d, %s, %d, %d>", d, cs, m,
                                          m == kDense ? g : 1);
-                            else if (d <= 128 && (m != kVarlen || !c))
+                            else if ((d <= 128 && (m != kVarlen || !c)) || (d == 192 && m == kDense && !c))
                                 snprintf(out, 96, "fa_fwd_pp_kernel<%s, %d, %s, %d, %d>", e, d, cs, m,
                                          m == kDense ? g : 1);
                             else
