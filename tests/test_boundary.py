@@ -114,6 +114,9 @@ def test_kernel_name():
     """The dispatch's kernel, named as the profiler reports it; "" for sizes fa_fwd rejects."""
     assert fa.fa_fwd_kernel_name(4, 16, 4096, 128, 0, 1, 256) == "fa_fwd_pp_kernel<Bf16, 128, false, 0, 1>"
     assert fa.fa_fwd_kernel_name(4, 8, 4096, 256, 1, 2, 256) == "fa_fwd_mfma_kernel<F16, 256, true, 0>"
+    # D = 192: the ping-pong kernel without the causal mask, the one-barrier kernel with it
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 192, 0, 1, 256) == "fa_fwd_pp_kernel<Bf16, 192, false, 0, 1>"
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 192, 1, 1, 256) == "fa_fwd_mfma_kernel<Bf16, 192, true, 0>"
     assert fa.fa_fwd_kernel_name(1, 1, 128, 64, 0, 0, 256).startswith("fa_fwd_f32_kernel<64, false")
     # small grids take key groups: B2 H8 N1024 is 64 workgroups of 256 rows on 256 CUs
     assert fa.fa_fwd_kernel_name(2, 8, 1024, 64, 1, 1, 256) == "fa_fwd_pp_kernel<Bf16, 64, true, 0, 4>"
