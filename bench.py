@@ -280,7 +280,17 @@ def bench_one(name, steps, warmup, copy_calibration=False, flush=False, warm_sec
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     kernel = fa.fa_fwd_kernel_name(B, H, N, D, int(causal), code, n_cus)
     if split:
-        kernel = "%s (%d splits) + fa_merge_kernel" % (kernel.replace(", 0>", ", 1>"), n_splits)
+        # the key split's instance (mode 1, one key group): the ping-pong kernel at
+        # D <= 128, the one-barrier kernel above, the fp32 kernel for fp32
+        cs = "true" if causal else "false"
+        e = {"bf16": "Bf16", "f16": "F16"}.get(dtype)
+        if dtype == "f32":
+            kernel = "fa_fwd_f32_kernel<%d, %s, 1, 1>" % (D, cs)
+        elif D <= 128:
+            kernel = "fa_fwd_pp_kernel<%s, %d, %s, 1, 1>" % (e, D, cs)
+        else:
+            kernel = "fa_fwd_mfma_kernel<%s, %d, %s, 1>" % (e, D, cs)
+        kernel = "%s (%d splits) + fa_merge_kernel" % (kernel, n_splits)
     res = dict(name=name, B=B, H=H, N=N, D=D, dtype=dtype, causal=causal, ms_per_step=ms_per_step,
                kernel_ms=kern_ms, kernel_min_ms=per[0], kernel_median_ms=per[len(per) // 2], value=value,
                achieved=achieved, peak=peak, flops=flops, kernel=kernel, warmup_steps_run=n_warm)
