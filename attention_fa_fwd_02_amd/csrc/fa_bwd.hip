@@ -817,16 +817,17 @@ __global__ __launch_bounds__(512) void fa_bwd_dkdv8_kernel(BwdArgs a) {
                 s = E::mfma(lds_u32x4(qs + 32 * cc), kf[cc], s);
                 dp = E::mfma(lds_u32x4(ds + 32 * cc), lds_u32x4(vs + 32 * cc), dp);
             }
-            // three reads ahead, then per MFMA its reads (one for S, two for dP)
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            // the reads of six MFMAs ahead (nine), then per MFMA its reads (one for
+            // S, two for dP)
+            __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
-            for (int n = 0; n < 2 * DC - 2; ++n) {
+            for (int n = 0; n < 2 * DC - 6; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if (n % 2 == 1)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
             __builtin_amdgcn_sched_barrier(0);
             // P = exp2(c2 s - log2(e) lse_i), dS = P (dP - Delta_i); causal: a
             // query before the key gets P = 0.  Entry i of lane (r, g) is query
@@ -867,14 +868,14 @@ __global__ __launch_bounds__(512) void fa_bwd_dkdv8_kernel(BwdArgs a) {
                     dva[b] = E::mfma(tr_read(dt + off, P), pv, dva[b]);
                     dka[b] = E::mfma(tr_read(qt + off, P), sv, dka[b]);
                 }
-            // the transposing reads of four MFMAs ahead, then two after each MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            // the transposing reads of eight MFMAs ahead, then two after each MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
-            for (int n = 0; n < 4 * OB - 4; ++n) {
+            for (int n = 0; n < 4 * OB - 8; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
         wait_vmcnt<0>();
         tile_barrier();
