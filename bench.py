@@ -512,14 +512,15 @@ def main():
             for name in ("bwd", "bwd_causal"):
                 bench_bwd(name, ns, nw)
             for name in SPLIT_WORKLOADS:
-                bench_one(name, ns, nw, warm_seconds=0.5)
+                bench_one(name, ns, nw, warm_seconds=min(args.warm_seconds, 0.5))
             for name in ("varlen", "varlen_causal"):
                 bench_varlen(name, ns, nw)
             for name in ("fp8", "fp8_causal"):
                 bench_fp8(name, ns, nw)
         for name in WORKLOADS:
             if name != args.workload:
-                bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5), warm_seconds=0.5)
+                bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5),
+                          warm_seconds=min(args.warm_seconds, 0.5))
         for name in ("bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
                      "bwd_d256_causal", "bwd_f32", "bwd_f32_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
