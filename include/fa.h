@@ -73,6 +73,13 @@ typedef struct ihipStream_t *fa_stream_t;
  * and keeps no state beyond a per-device cache of the device architecture.
  * Calls on different streams may run concurrently.
  *
+ * Graph capture: a call enqueues kernel launches only (no allocation, no
+ * memset, no synchronisation), so once one call of the entry point has run
+ * on the device (the first call looks up device properties and raises the
+ * LDS limit of the larger kernels), later calls may be captured into a HIP
+ * graph; each replay recomputes from the captured buffers' current contents.
+ * The same holds for every entry point below.
+ *
  * Errors: every argument check is made on the host before any HIP call;
  * FA_ERR_INVALID_ARG for a NULL pointer, B/H/N < 1, D < 1, a non-finite
  * scale, causal not 0/1, an unknown dtype, q/k/v/o not 16-byte aligned,
