@@ -458,8 +458,9 @@ def main():
                     help="also time the headline, both modes, with caches flushed before every call (stderr)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(each (batch, head) slice is independent; see DESIGN.md for how it would shard)",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(each (batch, head) slice is independent, so the work would shard by slice, "
+              "or by key range with the lse merge)",
               file=sys.stderr)
         sys.exit(2)
     import torch
