@@ -42,7 +42,7 @@ typedef enum {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* an argument breaks the contract below */
-    FA_ERR_UNSUPPORTED = 2, /* well-formed but outside what this build implements */
+    FA_ERR_UNSUPPORTED = 2, /* well-formed but outside what the library implements */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error (device query or launch) */
 } fa_status;
 
