@@ -189,6 +189,14 @@ def test_headline_sampled(causal):
     check_case(w["B"], w["H"], w["N"], w["D"], "bf16", causal, w["seed"], n_rows=256, row_seed=11)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_headline_shape_other_dtypes(dtype, causal):
+    # the headline shape in the other two input types (same seed and recipe)
+    w = _w("headline_bf16")
+    check_case(w["B"], w["H"], w["N"], w["D"], dtype, causal, w["seed"], n_rows=128, row_seed=15)
+
+
 def test_wide_sampled():
     w = _w("wide_bf16")
     slices = fi.sample_slices(w["B"], w["H"], 8, seed=12)
