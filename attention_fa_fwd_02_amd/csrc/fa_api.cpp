@@ -19,12 +19,12 @@ hipError_t g_arch_err[kMaxDevices];
 
 size_t elem_size(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
-// Head dims of the forward kernels: 64 and 128 for fp32; 64, 96, 128, 192 and
-// 256 for bf16 / fp16.
+// Head dims of the forward kernels: 64 and 128 for fp32; every multiple of 32
+// from 32 to 256 for bf16 / fp16 (the backward takes the same sets).
 bool fwd_head_dim_ok(int64_t D, int dtype) {
     if (D == 64 || D == 128)
         return true;
-    return dtype != FA_DTYPE_F32 && (D == 96 || D == 192 || D == 256);
+    return dtype != FA_DTYPE_F32 && D >= 32 && D <= 256 && D % 32 == 0;
 }
 
 bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
@@ -136,9 +136,8 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim outside 64/96/128/192/256 (64/128 for fp32), "
-               "problem too large for "
-               "one launch, too many "
+        return "unsupported (head dim not a multiple of 32 in 32..256 (64/128 for fp32, "
+               "64/96/128/192/256 for FP8), problem too large for one launch, too many "
                "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
                "device is not gfx950)";
     case FA_ERR_HIP:
@@ -451,7 +450,7 @@ fa_status fa_check_bwd_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (dtype == FA_DTYPE_F32 ? (D != 64 && D != 128) : (D != 64 && D != 96 && D != 128 && D != 192 && D != 256))
+    if (!fwd_head_dim_ok(D, dtype))
         return FA_ERR_UNSUPPORTED;
     // B, H < 2^31 keep B * H (< 2^62) exact; the products are then compared
     // against their limits without being formed

@@ -996,12 +996,18 @@ hipError_t launch_bwd_t(bool causal, int64_t BH, const BwdArgs &args, hipStream_
 
 template <typename E>
 hipError_t launch_bwd_e(int D, bool causal, int64_t BH, const BwdArgs &args, hipStream_t stream) {
+    if (D == 32)
+        return launch_bwd_t<E, 32>(causal, BH, args, stream);
     if (D == 64)
         return launch_bwd_t<E, 64>(causal, BH, args, stream);
     if (D == 96)
         return launch_bwd_t<E, 96>(causal, BH, args, stream);
+    if (D == 160)
+        return launch_bwd_t<E, 160>(causal, BH, args, stream);
     if (D == 192)
         return launch_bwd_t<E, 192>(causal, BH, args, stream);
+    if (D == 224)
+        return launch_bwd_t<E, 224>(causal, BH, args, stream);
     if (D == 256)
         return launch_bwd_t<E, 256>(causal, BH, args, stream);
     return launch_bwd_t<E, 128>(causal, BH, args, stream);

@@ -1398,14 +1398,20 @@ hipError_t launch_mfma(bool causal, int64_t nwg, const FwdArgs &args, hipStream_
 template <typename E, int MODE>
 hipError_t launch_mfma_d(int D, bool causal, int64_t nwg, const FwdArgs &args, hipStream_t stream, int kg) {
     switch (D) {
+    case 32:
+        return launch_mfma<E, 32, MODE>(causal, nwg, args, stream, kg);
     case 64:
         return launch_mfma<E, 64, MODE>(causal, nwg, args, stream, kg);
     case 96:
         return launch_mfma<E, 96, MODE>(causal, nwg, args, stream, kg);
     case 128:
         return launch_mfma<E, 128, MODE>(causal, nwg, args, stream, kg);
+    case 160:
+        return launch_mfma<E, 160, MODE>(causal, nwg, args, stream, kg);
     case 192:
         return launch_mfma<E, 192, MODE>(causal, nwg, args, stream, kg);
+    case 224:
+        return launch_mfma<E, 224, MODE>(causal, nwg, args, stream, kg);
     default:
         return launch_mfma<E, 256, MODE>(causal, nwg, args, stream, kg);
     }
@@ -1454,12 +1460,13 @@ int choose_key_groups(int64_t BH, int64_t N, int64_t D, int dtype, int64_t n_cus
 const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg) {
     // every (dtype, head dim, causal, mode, key groups) the dispatch below can
     // reach, named as the profiler demangles the template instance
-    static char names[3][5][2][3][3][96];
+    constexpr int ND = 8;
+    static char names[3][ND][2][3][3][96];
     static std::once_flag once;
-    static const int dims[5] = {64, 96, 128, 192, 256};
+    static const int dims[ND] = {32, 64, 96, 128, 160, 192, 224, 256};
     std::call_once(once, [] {
         for (int t = 0; t < 3; ++t)
-            for (int di = 0; di < 5; ++di)
+            for (int di = 0; di < ND; ++di)
                 for (int c = 0; c < 2; ++c)
                     for (int m = 0; m < 3; ++m)
                         for (int gi = 0; gi < 3; ++gi) {
@@ -1470,7 +1477,8 @@ const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg)
                             if (t == 0)
                                 snprintf(out, 96, "fa_fwd_f32_kernel<%d, %s, %d, %d>", d, cs, m,
                                          m == kDense ? g : 1);
-                            else if ((d <= 128 && (m != kVarlen || !c)) || (d == 192 && m == kDense && !c))
+                            else if ((d <= 128 && (m != kVarlen || !c)) ||
+                                     ((d == 160 || d == 192) && m == kDense && !c))
                                 snprintf(out, 96, "fa_fwd_pp_kernel<%s, %d, %s, %d, %d>", e, d, cs, m,
                                          m == kDense ? g : 1);
                             else
@@ -1478,7 +1486,7 @@ const char *fwd_kernel_name(int dtype, int D, bool causal, FwdMode mode, int kg)
                         }
     });
     int di = -1;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < ND; ++i)
         if (dims[i] == D)
             di = i;
     const int gi = kg == 4 ? 2 : kg == 2 ? 1 : 0;

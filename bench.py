@@ -53,6 +53,9 @@ WORKLOADS = {
     "d256_causal": (4, 8, 4096, 256, "bf16", True, (1.0, 1.0, 1.0)),
     "d96": (4, 16, 4096, 96, "bf16", False, (1.0, 1.0, 1.0)),
     "d192": (4, 8, 4096, 192, "bf16", False, (1.0, 1.0, 1.0)),
+    "d32": (4, 16, 4096, 32, "bf16", False, (1.0, 1.0, 1.0)),
+    "d160": (4, 8, 4096, 160, "bf16", False, (1.0, 1.0, 1.0)),
+    "d224": (4, 8, 4096, 224, "bf16", False, (1.0, 1.0, 1.0)),
     "few_heads": (1, 2, 8192, 128, "bf16", False, (1.0, 1.0, 1.0)),
     "few_heads_causal": (1, 2, 8192, 128, "bf16", True, (1.0, 1.0, 1.0)),
 }
@@ -364,8 +367,9 @@ def bench_varlen(name, steps, warmup, warm_seconds=0.0):
 
 
 def bench_bwd(name, steps, warmup, warm_seconds=0.0):
-    """fa_bwd on the headline shape, at D = 96 for "bwd_d96*", B4 H8 N4096 at
-    D = 192 / 256 for "bwd_d192*" / "bwd_d256*", or the headline shape in fp32
+    """fa_bwd on the headline shape, at D = 32 / 96 for "bwd_d32*" / "bwd_d96*",
+    B4 H8 N4096 at D = 160 / 192 / 224 / 256 for "bwd_d160*" / "bwd_d192*" /
+    "bwd_d224*" / "bwd_d256*", or the headline shape in fp32
     for "bwd_f32*" (stderr line only).  FLOPs: the five contractions of the
     backward pass, 10*B*H*N^2*D (2.5x the forward's count, halved for causal);
     the kernels recompute S and dP once more (seven; eight at D = 256).
@@ -522,7 +526,7 @@ def main():
             if name != args.workload:
                 bench_one(name, max(10, args.steps // 5), max(10, args.warmup // 5),
                           warm_seconds=min(args.warm_seconds, 0.5))
-        for name in ("bwd_d96", "bwd_d96_causal", "bwd_d192", "bwd_d256",
+        for name in ("bwd_d32", "bwd_d96", "bwd_d96_causal", "bwd_d160", "bwd_d192", "bwd_d224", "bwd_d256",
                      "bwd_d256_causal", "bwd_f32", "bwd_f32_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
         for name in ("fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):

@@ -61,7 +61,7 @@ typedef struct ihipStream_t *fa_stream_t;
  *            with the natural-log logsumexp of row n's scaled scores,
  *            ln sum_j exp(scale * q_n . k_j) over the visible keys j.
  *   B, H, N  >= 1.
- *   D        head dimension: 64, 96, 128, 192 or 256 for bf16 / fp16; 64 or
+ *   D        head dimension: a multiple of 32 from 32 to 256 for bf16 / fp16; 64 or
  *            128 for fp32 (other values: FA_ERR_UNSUPPORTED).  Up to 192 a
  *            workgroup takes 256 query rows, above 192 it takes 128.
  *   scale    any finite float; usually 1/sqrt(D).  0 gives uniform weights.
@@ -382,8 +382,8 @@ uint64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  *   workspace         device pointer, 16-byte aligned, at least
  *                     fa_bwd_workspace_bytes(B, H, N, D) bytes; overwritten.
  *   B, H, N, D, scale, causal, stream  as for fa_fwd.
- *   dtype             FA_DTYPE_BF16 or FA_DTYPE_F16 (D = 64, 96, 128, 192,
- *                     256), or FA_DTYPE_F32 (D = 64 or 128; fp32 matrix
+ *   dtype             FA_DTYPE_BF16 or FA_DTYPE_F16 (D a multiple of 32 from 32
+ *                     to 256), or FA_DTYPE_F32 (D = 64 or 128; fp32 matrix
  *                     instructions, every intermediate in fp32).
  *
  * Errors: FA_ERR_INVALID_ARG for a NULL pointer, B/H/N/D < 1, a non-finite

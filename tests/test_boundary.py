@@ -87,7 +87,8 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(D=32), dict(D=80), dict(D=160), dict(D=512), dict(D=96, dtype=0), dict(D=256, dtype=0),
+    dict(D=16), dict(D=48), dict(D=80), dict(D=288), dict(D=512), dict(D=96, dtype=0), dict(D=256, dtype=0),
+    dict(D=32, dtype=0), dict(D=160, dtype=0),
     dict(N=1 << 30), dict(B=1 << 20, H=1 << 10, N=1 << 7), dict(B=1 << 15, H=1 << 8, N=257),
     # head dims above 192 use 128-row query blocks: 2^16 * 2^7 blocks of 128 rows
     dict(B=1 << 16, H=1 << 0, N=128 * 128, D=256, q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T),
@@ -97,7 +98,7 @@ def test_unsupported(kw):
 
 
 @pytest.mark.parametrize("dtype", [1, 2])
-@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 192, 224, 256])
 def test_head_dims_16bit(D, dtype):
     assert check(D=D, dtype=dtype) == fa.FA_OK
 
@@ -117,6 +118,14 @@ def test_kernel_name():
     # D = 192: the ping-pong kernel without the causal mask, the one-barrier kernel with it
     assert fa.fa_fwd_kernel_name(4, 8, 4096, 192, 0, 1, 256) == "fa_fwd_pp_kernel<Bf16, 192, false, 0, 1>"
     assert fa.fa_fwd_kernel_name(4, 8, 4096, 192, 1, 1, 256) == "fa_fwd_mfma_kernel<Bf16, 192, true, 0>"
+    # D = 160 like 192; D = 32 like 64 (key groups included)
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 160, 0, 2, 256) == "fa_fwd_pp_kernel<F16, 160, false, 0, 1>"
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 160, 1, 1, 256) == "fa_fwd_mfma_kernel<Bf16, 160, true, 0>"
+    assert fa.fa_fwd_kernel_name(4, 16, 4096, 32, 1, 1, 256) == "fa_fwd_pp_kernel<Bf16, 32, true, 0, 1>"
+    assert fa.fa_fwd_kernel_name(2, 8, 1024, 32, 0, 1, 256) == "fa_fwd_pp_kernel<Bf16, 32, false, 0, 4>"
+    # D = 224 like 256: four waves, the one-barrier kernel in every mode
+    assert fa.fa_fwd_kernel_name(4, 8, 4096, 224, 0, 1, 256) == "fa_fwd_mfma_kernel<Bf16, 224, false, 0>"
+    assert fa.fa_fwd_kernel_name(1, 1, 128, 32, 0, 0, 256) == ""
     assert fa.fa_fwd_kernel_name(1, 1, 128, 64, 0, 0, 256).startswith("fa_fwd_f32_kernel<64, false")
     # small grids take key groups: B2 H8 N1024 is 64 workgroups of 256 rows on 256 CUs
     assert fa.fa_fwd_kernel_name(2, 8, 1024, 64, 1, 1, 256) == "fa_fwd_pp_kernel<Bf16, 64, true, 0, 4>"
@@ -399,7 +408,7 @@ def test_bwd_workspace_bytes():
 def test_bwd_good_arguments_pass():
     assert bcheck() == fa.FA_OK and bcheck(arch=None) == fa.FA_OK
     for dt in (1, 2):
-        for D in (64, 96, 128, 192, 256):
+        for D in (32, 64, 96, 128, 160, 192, 224, 256):
             for c in (0, 1):
                 assert bcheck(dtype=dt, D=D, causal=c) == fa.FA_OK
     for D in (64, 128):
@@ -418,7 +427,8 @@ def test_bwd_invalid_arguments(kw):
     assert bcheck(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=0, D=96), dict(dtype=0, D=256), dict(D=80), dict(D=160), dict(D=512),
+@pytest.mark.parametrize("kw", [dict(dtype=0, D=96), dict(dtype=0, D=256), dict(dtype=0, D=32), dict(dtype=0, D=160),
+                                dict(D=48), dict(D=80), dict(D=288), dict(D=512),
                                 dict(N=1 << 30),
                                 dict(B=1 << 14, H=1 << 6, N=128 * 8, wsb=1 << 62)])
 def test_bwd_unsupported(kw):

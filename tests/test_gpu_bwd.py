@@ -125,7 +125,7 @@ def term_magnitudes(q, k, v, do, sc, causal, o_dev):
 
 
 @pytest.mark.parametrize("N", [1, 31, 64, 100, 255, 257, 600])
-@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 192, 224, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ragged(N, D, dtype, causal):

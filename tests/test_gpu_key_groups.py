@@ -39,7 +39,7 @@ KG4 = [(2, 8, 1024), (1, 3, 100), (2, 2, 129), (1, 1, 1000)]
 # (dtype, D) pairs: every 16-bit head dim of the kernel; fp32 at D = 64 (key
 # groups) and, with whole tiles only, D = 128
 DT_KG1 = [("bf16", 64), ("bf16", 96), ("bf16", 128), ("f32", 64), ("f32", 128)]
-DT_KG = [(t, d) for t in ("bf16", "f16") for d in (64, 96, 128)] + [("f32", 64)]
+DT_KG = [(t, d) for t in ("bf16", "f16") for d in (32, 64, 96, 128)] + [("f32", 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True])

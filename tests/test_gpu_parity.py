@@ -273,7 +273,7 @@ def test_side_stream_and_binding():
 # ---------------------------------------------------------------- head dims
 
 @pytest.mark.parametrize("N", [1, 100, 129, 300, 1000])
-@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_dims(N, D, dtype, causal):

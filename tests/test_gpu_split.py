@@ -124,7 +124,7 @@ def test_split_parity(N, n_splits, D, dtype, causal):
     check_split(2, 3, N, D, dtype, causal, n_splits, seed=300 + N + D)
 
 
-@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_split_head_dims(D, causal):
     check_split(2, 3, 1000, D, "bf16", causal, 3, seed=350 + D)

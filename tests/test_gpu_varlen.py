@@ -108,7 +108,7 @@ def test_varlen_cross(D, dtype, causal):
     check_varlen(MIX_Q, MIX_K, 2, D, dtype, causal, seed=600 + D)
 
 
-@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_head_dims(D, causal):
     check_varlen(MIX_Q, MIX_K, 2, D, "bf16", causal, seed=650 + D)
