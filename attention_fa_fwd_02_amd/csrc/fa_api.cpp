@@ -136,8 +136,8 @@ const char *fa_status_string(int status) {
         return "invalid argument (null pointer, non-positive size, non-finite scale, bad causal or "
                "dtype, misaligned pointer, or outputs overlapping inputs)";
     case FA_ERR_UNSUPPORTED:
-        return "unsupported (head dim not a multiple of 32 in 32..256 (64/128 for fp32, "
-               "64/96/128/192/256 for FP8), problem too large for one launch, too many "
+        return "unsupported (head dim not a multiple of 32 in 32..256 (64/128 for fp32), "
+               "problem too large for one launch, too many "
                "key splits or merge parts, merge head dim not a multiple of 8 in 8..512, or "
                "device is not gfx950)";
     case FA_ERR_HIP:
@@ -370,7 +370,7 @@ fa_status fa_check_fp8_args(const void *q, const void *k, const void *v, const v
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)lse & 3u)
         return FA_ERR_INVALID_ARG;
-    if (D != 64 && D != 96 && D != 128 && D != 192 && D != 256)
+    if (D < 32 || D > 256 || D % 32 != 0)
         return FA_ERR_UNSUPPORTED;
     // V^T rows are addressed with 32-bit offsets: D * Npad < 2^32
     if (N >= (int64_t(1) << 24) || B >= (int64_t(1) << 31) || H >= (int64_t(1) << 31))

@@ -111,8 +111,9 @@ struct F8Cfg {
     static constexpr int KP = D + 16;        // K row pitch (bytes)
     static constexpr int VTP = BC + 16;      // V^T row pitch (bytes)
     static constexpr int NK = BC * KP / 1024;
-    // 1 KB blocks of a V^T tile; at D = 96 the last block is half spare (its
-    // slots lie past the last feature row and read zeros)
+    // 1 KB blocks of a V^T tile; when D is an odd multiple of 32 the last
+    // block is half spare (its slots lie past the last feature row and read
+    // zeros)
     static constexpr int NV = (D * VTP + 1023) / 1024;
     static_assert(NK * 1024 == BC * KP, "K tiles are whole 1 KB blocks");
     static constexpr int LPW = (NK + NV + kF8Waves - 1) / kF8Waves; // loads per wave and tile
@@ -122,8 +123,9 @@ struct F8Cfg {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF8Threads) void fa_fwd_fp8_kernel(Fp8Args a) {
     using Cfg = F8Cfg<D>;
-    // DS 64-wide k-steps of the score MFMA; at D = 96 the second step's upper
-    // half (features 96 .. 127, lane half g = 1) has a zero Q operand
+    // DS 64-wide k-steps of the score MFMA; when D is an odd multiple of 32 the
+    // last step's upper half (features D .. D + 31, lane half g = 1) has a zero
+    // Q operand
     constexpr int BC = Cfg::BC, KB = BC / 32, DS = (D + 63) / 64, OB = D / 32;
     constexpr bool HALF_STEP = D % 64 != 0;
     static_assert(D % 32 == 0, "features in 32-wide MFMA blocks");
@@ -525,12 +527,18 @@ hipError_t launch_fp8_t(bool causal, int64_t BH, const Fp8Args &args, hipStream_
 
 hipError_t launch_fp8(int D, bool causal, int64_t BH, const Fp8Args &args, hipStream_t stream) {
     switch (D) {
+    case 32:
+        return launch_fp8_t<32>(causal, BH, args, stream);
     case 64:
         return launch_fp8_t<64>(causal, BH, args, stream);
     case 96:
         return launch_fp8_t<96>(causal, BH, args, stream);
+    case 160:
+        return launch_fp8_t<160>(causal, BH, args, stream);
     case 192:
         return launch_fp8_t<192>(causal, BH, args, stream);
+    case 224:
+        return launch_fp8_t<224>(causal, BH, args, stream);
     case 256:
         return launch_fp8_t<256>(causal, BH, args, stream);
     default:

@@ -409,7 +409,7 @@ def bench_bwd(name, steps, warmup, warm_seconds=0.0):
 
 def bench_fp8(name, steps, warmup, warm_seconds=0.0):
     """fa_fwd_fp8 on the headline shape (B4 H16 N4096 D128, E4M3 inputs, bf16 O),
-    or B4 H8 N4096 at head dim 96 / 192 / 256 (stderr line only).  FLOPs as for
+    or B4 H8 N4096 at another head dim (stderr line only).  FLOPs as for
     the 16-bit path; peak: dense FP8 MFMA."""
     import numpy as np
     import torch
@@ -529,7 +529,7 @@ def main():
         for name in ("bwd_d32", "bwd_d96", "bwd_d96_causal", "bwd_d160", "bwd_d192", "bwd_d224", "bwd_d256",
                      "bwd_d256_causal", "bwd_f32", "bwd_f32_causal"):
             bench_bwd(name, max(10, args.steps // 5), max(10, args.warmup // 5))
-        for name in ("fp8_d96", "fp8_d192", "fp8_d256", "fp8_d256_causal"):
+        for name in ("fp8_d32", "fp8_d96", "fp8_d160", "fp8_d192", "fp8_d224", "fp8_d256", "fp8_d256_causal"):
             bench_fp8(name, max(10, args.steps // 5), max(10, args.warmup // 5))
     if args.flush:
         for name in ("headline", "headline_causal"):

@@ -327,7 +327,7 @@ uint64_t fa_fwd_fp8_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  *   lse         device pointer, [B, H, N] fp32, overwritten (natural-log
  *               logsumexp of scale * (q q_descale) . (k k_descale)).
  *   B, H, N     >= 1, N < 2^24.
- *   D           64, 96, 128, 192 or 256.
+ *   D           a multiple of 32 from 32 to 256.
  *   scale, q_descale, k_descale, v_descale  finite floats.
  *   causal      0 or 1 (key j visible to query i iff j <= i).
  *   workspace   device pointer, 16-byte aligned, at least
@@ -336,7 +336,7 @@ uint64_t fa_fwd_fp8_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  * Errors: FA_ERR_INVALID_ARG for a NULL pointer, B/H/N/D < 1, a non-finite
  * scale or descale, causal not 0/1, misalignment, a workspace too small, or
  * outputs / workspace overlapping each other or an input; FA_ERR_UNSUPPORTED
- * for D other than 64/96/128/192/256, N >= 2^24, B*H >= 2^16, the size limits of
+ * for D not a multiple of 32 in 32..256, N >= 2^24, B*H >= 2^16, the size limits of
  * fa_fwd, or a device that is not gfx950; FA_ERR_HIP when a device query or
  * a launch fails.  All checks precede any HIP call; the library allocates
  * nothing.

@@ -463,7 +463,7 @@ def test_fp8_workspace_bytes():
 
 def test_fp8_good_arguments_pass():
     assert f8check() == fa.FA_OK and f8check(arch=None) == fa.FA_OK
-    for D in (64, 96, 128, 192, 256):
+    for D in (32, 64, 96, 128, 160, 192, 224, 256):
         assert f8check(D=D, wsb=1 << 40) == fa.FA_OK
     assert f8check(D=64, causal=1, scale=-0.3, qd=-1.0) == fa.FA_OK
 
@@ -478,6 +478,6 @@ def test_fp8_invalid_arguments(kw):
     assert f8check(**kw) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(D=80), dict(D=32), dict(D=512), dict(N=1 << 24), dict(B=1 << 8, H=1 << 8)])
+@pytest.mark.parametrize("kw", [dict(D=80), dict(D=16), dict(D=288), dict(D=512), dict(N=1 << 24), dict(B=1 << 8, H=1 << 8)])
 def test_fp8_unsupported(kw):
     assert f8check(**kw, wsb=1 << 62) == fa.FA_ERR_UNSUPPORTED

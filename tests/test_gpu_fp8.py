@@ -91,20 +91,20 @@ def torch_idx(rows):
 
 
 @pytest.mark.parametrize("N", [1, 100, 128, 129, 300, 1000])
-@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 160, 192, 224, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_ragged(N, D, causal):
     check_fp8(2, 3, N, D, causal, seed=900 + N + D)
 
 
-@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
 def test_fp8_head_dims_descales(D):
     """The head dims beyond 64/128 with non-unit descales and a negative scale."""
     for causal in (False, True):
         check_fp8(1, 2, 700, D, causal, seed=970 + D, scale=-0.7 / math.sqrt(D), descale=(0.5, 2.0, 1.5))
 
 
-@pytest.mark.parametrize("D", [96, 192, 256])
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 224, 256])
 def test_fp8_head_dims_sampled(D):
     """B4 H8 N4096 at each added head dim: 96 sampled rows of 6 seeded slices."""
     slices = fi.sample_slices(4, 8, 6, seed=17)
